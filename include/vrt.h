@@ -1,0 +1,217 @@
+/*
+ * vrt.h - streamed windowed-causal attention for MI355X (gfx950), C ABI.
+ *
+ * What the library computes
+ * -------------------------
+ * The hot path of a streaming audio encoder (Voxtral Realtime family doc,
+ * "Architecture (summary)" and the Capability Validation table, Streaming
+ * row): each feed of new encoder frames is rotated with NEOX RoPE
+ * (theta 1e6, head_dim 64) at absolute positions, its K/V are appended to a
+ * per-layer 1536-slot ring, the ring is compacted to its last 750 frames when
+ * it would overflow, and every new query attends only to keys whose absolute
+ * position p' satisfies p - 750 < p' <= p (streaming-plan page, "SHIPPED"
+ * section, "Mechanism" and "Unbounded length" paragraphs).  The decoder's
+ * one-token step (GQA 32 query / 8 kv heads, head_dim 128, window 8192,
+ * modulo ring) runs on the same kernels (family doc, Decoder bullet;
+ * Streaming row item 5).
+ *
+ * State is injected (bunsen book, "Stateless modules and streaming
+ * contexts", "The principle: state is injected" and "The pattern"): the
+ * caller owns every byte of device memory, creates one state per stream (one
+ * state holds all layers of that stream, like a multi-layer KV cache), and
+ * passes the states back on every call.  One call may carry many states
+ * (streams are written one at a time and read together: same chapter, "The
+ * write_read fold").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All device pointers are caller-owned; the library never allocates or
+ *   frees device memory and holds no global state.  All device work is
+ *   enqueued on the caller's `stream` and is asynchronous.
+ * - Arguments are checked before anything is enqueued.  On any error nothing
+ *   is enqueued and no state changes (streaming-plan page, "Per-hook
+ *   behavior": validate is pure).
+ * - Host metadata (abs_base, n_kv per layer) advances when work is enqueued;
+ *   it is a deterministic function of the calls, so no device-to-host sync is
+ *   ever needed.
+ * - If a kernel launch reports an error, VRT_ERR_DEVICE is returned and every
+ *   state in the call is marked poisoned; poisoned states refuse every call
+ *   (VRT_ERR_POISONED) until vrt_stream_state_reset.
+ * - Absolute positions are int64 and must stay in [0, 2^53).
+ * - Tensors are contiguous, row-major, in the state's dtype (float32 or
+ *   bfloat16 bit patterns), 256-byte aligned device pointers.
+ */
+#ifndef VRT_H
+#define VRT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VRT_OK = 0,
+    VRT_ERR_INVALID = 1,      /* bad argument: null pointer, size, range, mixed descs */
+    VRT_ERR_UNSUPPORTED = 2,  /* a configuration the library does not build */
+    VRT_ERR_CAPACITY = 3,     /* memory or size too small for the request */
+    VRT_ERR_DEVICE = 4,       /* a HIP launch failed; involved states are poisoned */
+    VRT_ERR_POISONED = 5      /* state was poisoned by an earlier device error */
+} vrt_status;
+
+typedef enum { VRT_F32 = 0, VRT_BF16 = 1 } vrt_dtype;
+
+typedef enum {
+    VRT_ENC_RING = 0,     /* encoder: contiguous ring + compaction */
+    VRT_DEC_MODRING = 1   /* decoder: slot = position % ring_slots */
+} vrt_cache_kind;
+
+/* Everything about a cache is fixed when its states are created
+ * (bunsen book, "Known gaps": invalid configurations fail at construction).
+ * Encoder on the pages: kind ENC_RING, 20 heads (q = kv), head_dim 64,
+ * window 750, ring_slots 1536, max_batch 512, rope_theta 1e6, 32 layers.
+ * Decoder: kind DEC_MODRING, 32 q / 8 kv heads, head_dim 128,
+ * window = ring_slots = 8192, rope_theta 1e6, 26 layers. */
+typedef struct {
+    int32_t kind;        /* vrt_cache_kind */
+    int32_t dtype;       /* vrt_dtype: storage and I/O type; accumulation is fp32 */
+    int32_t n_layers;    /* layers held by one state (>= 1) */
+    int32_t n_heads_q;   /* query heads (multiple of n_heads_kv) */
+    int32_t n_heads_kv;  /* key/value heads */
+    int32_t head_dim;    /* 64 or 128 */
+    int32_t window;      /* W: a query at p sees keys in (p - W, p] */
+    int32_t ring_slots;  /* ENC: >= window + max_batch; DEC: >= window, multiple of 64 */
+    int32_t max_batch;   /* ENC: largest sub-batch per append (feeds are split) */
+    int32_t reserved;    /* must be 0 */
+    double rope_theta;   /* NEOX RoPE base; omega_i = theta^(-2i/head_dim) */
+} vrt_cache_desc;
+
+/* Opaque host object: desc, per-layer abs_base / n_kv, the device memory it
+ * was given.  It owns no device memory. */
+typedef struct vrt_stream_state vrt_stream_state;
+
+const char* vrt_status_str(vrt_status s);
+const char* vrt_version(void);
+
+/* Text of the last HIP error that a launch made by this library reported on
+ * the calling thread ("" if none).  Diagnostics only; the pointer stays valid
+ * until the next failing launch on the same thread. */
+const char* vrt_last_device_error(void);
+
+/* Check a descriptor without creating anything.  VRT_ERR_INVALID for
+ * non-positive sizes or a reserved field != 0; VRT_ERR_UNSUPPORTED for a
+ * head_dim other than 64/128, an unknown dtype/kind, an encoder ring smaller
+ * than window + max_batch (streaming-plan page, "Unbounded length": batches
+ * of at most 512 frames so one feed can never overflow the 1536-slot ring),
+ * or a decoder ring smaller than the window or not a multiple of 64. */
+vrt_status vrt_desc_check(const vrt_cache_desc* desc);
+
+/* Device bytes one state needs: for each layer a K ring and a V ring, each
+ * [n_heads_kv][ring_slots][head_dim] elements.  0 if the desc is invalid. */
+size_t vrt_state_device_bytes(const vrt_cache_desc* desc);
+
+/* Byte offset, inside a state's device memory, of row 0 of the ring slice
+ * (layer, which = 0 for K / 1 for V, kv head).  Rows are head_dim elements;
+ * slot s of that slice starts at offset + s * head_dim * elem_size.  K rows
+ * hold RoPE-rotated keys, V rows the values as given.  (size_t)-1 on bad
+ * arguments. */
+size_t vrt_ring_offset(const vrt_cache_desc* desc, int layer, int which, int kv_head);
+
+/* Create a state over caller memory `dev_mem` of `bytes` (>= the value of
+ * vrt_state_device_bytes; 256-byte aligned).  Every layer starts empty with
+ * abs_base = start_pos (the absolute position of the first frame that will
+ * be fed).  Nothing is written to dev_mem.  VRT_ERR_CAPACITY if bytes is too
+ * small.  The state must be destroyed with vrt_stream_state_destroy. */
+vrt_status vrt_stream_state_create(const vrt_cache_desc* desc, void* dev_mem, size_t bytes,
+                                   int64_t start_pos, vrt_stream_state** out);
+
+/* Clear the stream (every layer: n_kv = 0, abs_base = start_pos), keep the
+ * memory, clear the poisoned flag (streaming-plan page, "Per-hook behavior":
+ * reset clears streaming state and keeps allocations).  Host-only. */
+vrt_status vrt_stream_state_reset(vrt_stream_state* st, int64_t start_pos);
+
+void vrt_stream_state_destroy(vrt_stream_state* st);
+
+/* Host mirror of one layer's ring: abs_base = absolute position held in slot
+ * 0 (streaming-plan page, "Unbounded length": stream_enc_abs_base), n_kv =
+ * rows held.  For a decoder state abs_base is the stream's first position and
+ * n_kv counts every token written (slot of position p is p % ring_slots). */
+vrt_status vrt_stream_state_query(const vrt_stream_state* st, int layer, int64_t* abs_base,
+                                  int32_t* n_kv);
+
+/* Pure host planning of one encoder append, the rule every feed applies per
+ * (state, layer) before each sub-batch (streaming-plan page, "Unbounded
+ * length": contiguous writes, compaction keeping the last `window` frames
+ * when the ring would overflow, feeds split into <= max_batch sub-batches).
+ * Applies a feed of n_new frames to (*abs_base, *n_kv) in place and returns
+ * in *n_compactions how many compactions it implies.  No device work. */
+vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32_t* n_kv,
+                            int n_new, int32_t* n_compactions);
+
+/* Which attention path a sub-batch of n queries takes: 0 = VALU kernel,
+ * 1 = MFMA kernel.  A pure function of (dtype, n): fp32 always 0; bf16 takes
+ * 1 when n >= 32.  Results are bit-identical under any chunking that keeps
+ * every sub-batch on the same path. */
+int vrt_attn_path(const vrt_cache_desc* desc, int n);
+
+/* Offline windowed attention over one whole sequence (streaming-plan page,
+ * "Why offline == streaming" and the bounded-window re-encode section: the
+ * whole-clip encoder under the 750-frame windowed-causal mask).
+ * q [T][n_heads_q][head_dim], k/v [T][n_heads_kv][head_dim], out like q;
+ * positions are start_pos + t.  `scratch` (device, caller-owned, at least
+ * vrt_offline_scratch_bytes) receives the rotated keys and the values in
+ * head-major order.  Same kernels and arithmetic as the streamed path, so a
+ * streamed run on the same path is bit-identical to this call.
+ * Encoder descs only (VRT_ERR_INVALID otherwise). */
+size_t vrt_offline_scratch_bytes(const vrt_cache_desc* desc, int T);
+vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const void* k,
+                                const void* v, int T, int64_t start_pos, void* out,
+                                void* scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* One feed of n_new frames to layers [layer0, layer0 + n_layers) of each of
+ * n_states encoder states (streaming-plan page, "Mechanism": the chunk's K/V
+ * are written at rows [n_kv_before, n_kv_total) and the queries then read
+ * rows [0, n_kv_total) under the windowed mask).  Per (state, layer) and per
+ * sub-batch of <= max_batch frames: compaction if needed, RoPE + append,
+ * then attention of the sub-batch's queries (each new query also sees the
+ * earlier new frames of its feed).
+ * q/out: [n_states][n_layers][n_new][n_heads_q][head_dim];
+ * k/v:   [n_states][n_layers][n_new][n_heads_kv][head_dim].
+ * All states must share one desc (field-wise equal) and be distinct.
+ * VRT_ERR_INVALID on null pointers, n_new < 1, bad layer range, mixed descs,
+ * a repeated state, or a decoder state. */
+vrt_status vrt_enc_attn_feed(vrt_stream_state* const* states, int n_states, int layer0,
+                             int n_layers, const void* q, const void* k, const void* v,
+                             int n_new, void* out, hipStream_t stream);
+
+/* Compact layers [layer0, layer0 + n_layers) of each state now: keep the last
+ * `window` rows at the front (streaming-plan page, "Unbounded length": copy
+ * the last 750 frames to the front).  A no-op for a layer with
+ * n_kv <= window.  Encoder states only. */
+vrt_status vrt_ring_compact(vrt_stream_state* const* states, int n_states, int layer0,
+                            int n_layers, hipStream_t stream);
+
+/* Decoder attention for n_tok tokens per (state, layer) (family doc,
+ * Streaming row item 5: token cur is written to slot cur % ring_slots, RoPE
+ * positions stay absolute, the step reveals [cur - window + 1, cur]; GQA:
+ * query head h reads kv head h / (n_heads_q / n_heads_kv)).  n_tok = 1 is
+ * the decode step (split over keys, then a log-sum-exp merge in ascending
+ * key order); n_tok > 1 is a prefill (family doc: the 39-token prompt) and
+ * may not overwrite a slot that one of its own queries still needs
+ * (VRT_ERR_INVALID).
+ * q/out: [n_states][n_layers][n_tok][n_heads_q][head_dim]; k/v as for feed.
+ * `workspace` (device, caller-owned) must hold vrt_dec_workspace_bytes. */
+size_t vrt_dec_workspace_bytes(const vrt_cache_desc* desc, int n_states, int n_layers,
+                               int n_tok);
+vrt_status vrt_dec_attn_step(vrt_stream_state* const* states, int n_states, int layer0,
+                             int n_layers, const void* q, const void* k, const void* v,
+                             int n_tok, void* out, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VRT_H */

@@ -89,3 +89,22 @@ def windowed_fullmask(q, k, v, positions, window: int, theta: float) -> np.ndarr
             for i in range(d):
                 out[t, h, i] = sum(w[u] * v[u, g, i] for u in w) / z
     return out
+
+
+def windowed_at(q, k, v, start_pos: int, window: int, theta: float, ts) -> np.ndarray:
+    """Outputs of ``windowed`` for the query rows ``ts`` only, each computed
+    from its own gathered window (for sampled checks at sizes where the whole
+    sequence would take too long).  Returns [len(ts)][Hq][d] in fp64."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    group = q.shape[1] // k.shape[1]
+    out = []
+    for t in ts:
+        t = int(t)
+        u0 = max(0, t - window + 1)
+        pos = start_pos + np.arange(u0, t + 1, dtype=np.int64)
+        kr = rope.apply(np.asarray(k[u0:t + 1], dtype=np.float64), pos, theta)
+        qr = rope.apply(np.asarray(q[t:t + 1], dtype=np.float64), pos[-1:], theta)[0]
+        out.append(window_rows(qr, kr, np.asarray(v[u0:t + 1], dtype=np.float64), group))
+    return np.stack(out)

@@ -1,0 +1,250 @@
+"""Python binding of libvrt (the C ABI declared in include/vrt.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+Device buffers are passed as raw pointers; anything with a ``data_ptr()``
+method (a torch tensor on the GPU) or a plain int is accepted.  Streams are
+``hipStream_t`` handles as ints (``torch.cuda.current_stream().cuda_stream``),
+0 for the null stream.
+
+Importing this module loads ``libvrt.so`` from this directory and raises if
+it is missing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, byref, c_char_p, c_double, c_int, c_int32, c_int64, \
+    c_size_t, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvrt.so")
+
+F32, BF16 = 0, 1
+ENC_RING, DEC_MODRING = 0, 1
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE, ERR_POISONED = range(6)
+
+EXPORTS = (
+    "vrt_status_str", "vrt_version", "vrt_last_device_error", "vrt_desc_check", "vrt_state_device_bytes",
+    "vrt_ring_offset", "vrt_stream_state_create", "vrt_stream_state_reset",
+    "vrt_stream_state_destroy", "vrt_stream_state_query", "vrt_ring_advance", "vrt_attn_path",
+    "vrt_offline_scratch_bytes", "vrt_enc_attn_offline", "vrt_enc_attn_feed",
+    "vrt_ring_compact", "vrt_dec_workspace_bytes", "vrt_dec_attn_step",
+)
+
+
+class CacheDesc(Structure):
+    _fields_ = [
+        ("kind", c_int32), ("dtype", c_int32), ("n_layers", c_int32),
+        ("n_heads_q", c_int32), ("n_heads_kv", c_int32), ("head_dim", c_int32),
+        ("window", c_int32), ("ring_slots", c_int32), ("max_batch", c_int32),
+        ("reserved", c_int32), ("rope_theta", c_double),
+    ]
+
+
+def enc_desc(dtype=BF16, n_layers=1, heads=20, head_dim=64, window=750, ring_slots=1536,
+             max_batch=512, theta=1.0e6) -> CacheDesc:
+    """Encoder cache as on the pages: 20 heads x 64, window 750, 1536 slots."""
+    return CacheDesc(ENC_RING, dtype, n_layers, heads, heads, head_dim, window, ring_slots,
+                     max_batch, 0, theta)
+
+
+def dec_desc(dtype=BF16, n_layers=1, heads_q=32, heads_kv=8, head_dim=128, window=8192,
+             ring_slots=8192, max_batch=512, theta=1.0e6) -> CacheDesc:
+    """Decoder cache as on the pages: GQA 32/8, 128, window = ring = 8192."""
+    return CacheDesc(DEC_MODRING, dtype, n_layers, heads_q, heads_kv, head_dim, window,
+                     ring_slots, max_batch, 0, theta)
+
+
+class VrtError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = f"{what}: {status_str(status)} ({status})"
+        if status == ERR_DEVICE:
+            msg += f": {last_device_error()}"
+        super().__init__(msg)
+
+
+def _preload_hip_runtime():
+    """Use the HIP runtime PyTorch ships, when PyTorch is installed.
+
+    Two HIP runtimes in one process cannot share the GPU: the second one to
+    start sees no device.  PyTorch's ROCm wheel carries its own
+    libamdhip64.so (soname libamdhip64.so.7, the one libvrt.so needs), so
+    mapping that copy first makes both libraries bind to a single runtime,
+    whichever of them the program imports first.  PyTorch itself is not
+    imported here."""
+    import importlib.util
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.origin:
+        return None
+    path = os.path.join(os.path.dirname(spec.origin), "lib", "libamdhip64.so")
+    if os.path.exists(path):
+        ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+        return path
+    return None
+
+
+HIP_RUNTIME = None
+
+
+def _load():
+    global HIP_RUNTIME
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(there is no fallback path)")
+    HIP_RUNTIME = _preload_hip_runtime()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = c_void_p
+    sig = {
+        "vrt_status_str": (c_char_p, [c_int]),
+        "vrt_version": (c_char_p, []),
+        "vrt_last_device_error": (c_char_p, []),
+        "vrt_desc_check": (c_int, [POINTER(CacheDesc)]),
+        "vrt_state_device_bytes": (c_size_t, [POINTER(CacheDesc)]),
+        "vrt_ring_offset": (c_size_t, [POINTER(CacheDesc), c_int, c_int, c_int]),
+        "vrt_stream_state_create": (c_int, [POINTER(CacheDesc), P, c_size_t, c_int64, POINTER(P)]),
+        "vrt_stream_state_reset": (c_int, [P, c_int64]),
+        "vrt_stream_state_destroy": (None, [P]),
+        "vrt_stream_state_query": (c_int, [P, c_int, POINTER(c_int64), POINTER(c_int32)]),
+        "vrt_ring_advance": (c_int, [POINTER(CacheDesc), POINTER(c_int64), POINTER(c_int32), c_int,
+                                     POINTER(c_int32)]),
+        "vrt_attn_path": (c_int, [POINTER(CacheDesc), c_int]),
+        "vrt_offline_scratch_bytes": (c_size_t, [POINTER(CacheDesc), c_int]),
+        "vrt_enc_attn_offline": (c_int, [POINTER(CacheDesc), P, P, P, c_int, c_int64, P, P,
+                                         c_size_t, P]),
+        "vrt_enc_attn_feed": (c_int, [POINTER(P), c_int, c_int, c_int, P, P, P, c_int, P, P]),
+        "vrt_ring_compact": (c_int, [POINTER(P), c_int, c_int, c_int, P]),
+        "vrt_dec_workspace_bytes": (c_size_t, [POINTER(CacheDesc), c_int, c_int, c_int]),
+        "vrt_dec_attn_step": (c_int, [POINTER(P), c_int, c_int, c_int, P, P, P, c_int, P, P,
+                                      c_size_t, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_str(s: int) -> str:
+    return lib.vrt_status_str(s).decode()
+
+
+def version() -> str:
+    return lib.vrt_version().decode()
+
+
+def last_device_error() -> str:
+    return lib.vrt_last_device_error().decode()
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _check(s: int, what: str) -> None:
+    if s != OK:
+        raise VrtError(s, what)
+
+
+def desc_check(desc: CacheDesc) -> int:
+    return lib.vrt_desc_check(byref(desc))
+
+
+def state_device_bytes(desc: CacheDesc) -> int:
+    return lib.vrt_state_device_bytes(byref(desc))
+
+
+def ring_offset(desc: CacheDesc, layer: int, which: int, kv_head: int) -> int:
+    return lib.vrt_ring_offset(byref(desc), layer, which, kv_head)
+
+
+def attn_path(desc: CacheDesc, n: int) -> int:
+    return lib.vrt_attn_path(byref(desc), n)
+
+
+def ring_advance(desc: CacheDesc, abs_base: int, n_kv: int, n_new: int):
+    """Pure host planning of one encoder feed: (abs_base, n_kv, n_compactions)."""
+    b, k, c = c_int64(abs_base), c_int32(n_kv), c_int32(0)
+    _check(lib.vrt_ring_advance(byref(desc), byref(b), byref(k), n_new, byref(c)), "ring_advance")
+    return b.value, k.value, c.value
+
+
+class StreamState:
+    """One stream's multi-layer cache over caller-owned device memory."""
+
+    def __init__(self, desc: CacheDesc, dev_mem, nbytes: int, start_pos: int = 0):
+        self.desc = desc
+        self.mem = dev_mem          # keep the owner (e.g. a torch tensor) alive
+        h = c_void_p()
+        _check(lib.vrt_stream_state_create(byref(desc), _ptr(dev_mem), nbytes, start_pos,
+                                           byref(h)), "stream_state_create")
+        self.handle = h.value
+
+    def reset(self, start_pos: int) -> None:
+        _check(lib.vrt_stream_state_reset(self.handle, start_pos), "stream_state_reset")
+
+    def query(self, layer: int):
+        b, k = c_int64(), c_int32()
+        s = lib.vrt_stream_state_query(self.handle, layer, byref(b), byref(k))
+        if s not in (OK, ERR_POISONED):
+            _check(s, "stream_state_query")
+        return b.value, k.value
+
+    def close(self) -> None:
+        if self.handle:
+            lib.vrt_stream_state_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _handles(states):
+    arr = (c_void_p * len(states))(*[s.handle for s in states])
+    return arr
+
+
+def offline_scratch_bytes(desc: CacheDesc, T: int) -> int:
+    return lib.vrt_offline_scratch_bytes(byref(desc), T)
+
+
+def enc_attn_offline(desc, q, k, v, T, start_pos, out, scratch, scratch_bytes, stream=0):
+    _check(lib.vrt_enc_attn_offline(byref(desc), _ptr(q), _ptr(k), _ptr(v), T, start_pos,
+                                    _ptr(out), _ptr(scratch), scratch_bytes, stream),
+           "enc_attn_offline")
+
+
+def enc_attn_feed(states, layer0, n_layers, q, k, v, n_new, out, stream=0, check=True):
+    s = lib.vrt_enc_attn_feed(_handles(states), len(states), layer0, n_layers, _ptr(q), _ptr(k),
+                              _ptr(v), n_new, _ptr(out), stream)
+    if check:
+        _check(s, "enc_attn_feed")
+    return s
+
+
+def ring_compact(states, layer0, n_layers, stream=0):
+    _check(lib.vrt_ring_compact(_handles(states), len(states), layer0, n_layers, stream),
+           "ring_compact")
+
+
+def dec_workspace_bytes(desc, n_states, n_layers, n_tok) -> int:
+    return lib.vrt_dec_workspace_bytes(byref(desc), n_states, n_layers, n_tok)
+
+
+def dec_attn_step(states, layer0, n_layers, q, k, v, n_tok, out, workspace=None, ws_bytes=0,
+                  stream=0, check=True):
+    s = lib.vrt_dec_attn_step(_handles(states), len(states), layer0, n_layers, _ptr(q), _ptr(k),
+                              _ptr(v), n_tok, _ptr(out), _ptr(workspace), ws_bytes, stream)
+    if check:
+        _check(s, "dec_attn_step")
+    return s

@@ -1,0 +1,557 @@
+// C-ABI host side: argument checks, the host mirror of every ring, sub-batch
+// splitting, compaction decisions and launch planning.  Device work is only
+// enqueued after every check has passed; the mirrors advance as it is
+// enqueued, so no call ever reads anything back from the GPU.
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "vrt.h"
+#include "vrt_internal.h"
+
+struct vrt_stream_state {
+    vrt_cache_desc d;
+    char* dev;
+    size_t bytes;
+    std::vector<int64_t> abs_base;  // per layer: position held in slot 0 (decoder: first position)
+    std::vector<int32_t> n_kv;      // per layer: rows held (decoder: tokens written)
+    bool poisoned;
+};
+
+namespace {
+
+using namespace vrt;
+
+constexpr int64_t kPosLimit = (int64_t)1 << 53;
+
+// Text of the last HIP error a launch on this thread reported (diagnostics
+// only; read through vrt_last_device_error).
+thread_local char g_last_error[256] = "";
+
+hipError_t note(hipError_t e) {
+    if (e != hipSuccess) {
+        std::snprintf(g_last_error, sizeof g_last_error, "%s (%d)", hipGetErrorString(e), (int)e);
+    }
+    return e;
+}
+
+// A HIP error code is sticky per thread: an earlier failed runtime call made
+// by someone else would otherwise be reported after our own launch.  Clear it
+// once before a call enqueues anything.
+void clear_sticky_error() { (void)hipGetLastError(); }
+
+int elem_bytes(const vrt_cache_desc& d) { return d.dtype == VRT_BF16 ? 2 : 4; }
+
+bool same_desc(const vrt_cache_desc& a, const vrt_cache_desc& b) {
+    return a.kind == b.kind && a.dtype == b.dtype && a.n_layers == b.n_layers &&
+           a.n_heads_q == b.n_heads_q && a.n_heads_kv == b.n_heads_kv &&
+           a.head_dim == b.head_dim && a.window == b.window && a.ring_slots == b.ring_slots &&
+           a.max_batch == b.max_batch && a.rope_theta == b.rope_theta;
+}
+
+vrt_status check_desc(const vrt_cache_desc* d) {
+    if (!d) return VRT_ERR_INVALID;
+    if (d->reserved != 0) return VRT_ERR_INVALID;
+    if (d->kind != VRT_ENC_RING && d->kind != VRT_DEC_MODRING) return VRT_ERR_UNSUPPORTED;
+    if (d->dtype != VRT_F32 && d->dtype != VRT_BF16) return VRT_ERR_UNSUPPORTED;
+    if (d->n_layers < 1 || d->n_heads_q < 1 || d->n_heads_kv < 1 || d->window < 1 ||
+        d->ring_slots < 1 || d->max_batch < 1)
+        return VRT_ERR_INVALID;
+    if (d->n_heads_q % d->n_heads_kv != 0) return VRT_ERR_INVALID;
+    if (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta)) return VRT_ERR_INVALID;
+    if (d->head_dim != 64 && d->head_dim != 128) return VRT_ERR_UNSUPPORTED;
+    const int group = d->n_heads_q / d->n_heads_kv;
+    if (group > kRows) return VRT_ERR_UNSUPPORTED;
+    if (d->ring_slots > (1 << 24) || d->window > (1 << 24) || d->max_batch > (1 << 20))
+        return VRT_ERR_UNSUPPORTED;
+    if (d->kind == VRT_ENC_RING) {
+        if ((int64_t)d->ring_slots < (int64_t)d->window + d->max_batch) return VRT_ERR_UNSUPPORTED;
+    } else {
+        if (d->ring_slots < d->window || d->ring_slots % kTile != 0) return VRT_ERR_UNSUPPORTED;
+    }
+    return VRT_OK;
+}
+
+size_t slice_bytes(const vrt_cache_desc& d) {
+    return (size_t)d.ring_slots * d.head_dim * elem_bytes(d);
+}
+size_t layer_bytes(const vrt_cache_desc& d) { return 2 * (size_t)d.n_heads_kv * slice_bytes(d); }
+
+Geom make_geom(const vrt_cache_desc& d) {
+    Geom g;
+    g.dtype = d.dtype;
+    g.D = d.head_dim;
+    g.hq = d.n_heads_q;
+    g.hkv = d.n_heads_kv;
+    g.group = d.n_heads_q / d.n_heads_kv;
+    g.slots = d.ring_slots;
+    g.window = d.window;
+    g.mod = d.kind == VRT_DEC_MODRING ? 1 : 0;
+    g.slice_bytes = (long long)slice_bytes(d);
+    g.v_off = (long long)d.n_heads_kv * g.slice_bytes;
+    g.layer_bytes = 2 * g.v_off;
+    g.theta = d.rope_theta;
+    return g;
+}
+
+float scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
+
+// Common checks for the batched calls.  Pure: touches nothing.
+vrt_status check_batch(vrt_stream_state* const* st, int n_states, int layer0, int n_layers,
+                       int kind) {
+    if (!st || n_states < 1 || !st[0]) return VRT_ERR_INVALID;
+    const vrt_cache_desc& d = st[0]->d;
+    if (d.kind != kind) return VRT_ERR_INVALID;
+    if (layer0 < 0 || n_layers < 1 || layer0 > d.n_layers - n_layers) return VRT_ERR_INVALID;
+    std::vector<const vrt_stream_state*> seen;
+    seen.reserve(n_states);
+    for (int i = 0; i < n_states; ++i) {
+        if (!st[i]) return VRT_ERR_INVALID;
+        if (!same_desc(st[i]->d, d)) return VRT_ERR_INVALID;
+        seen.push_back(st[i]);
+    }
+    std::sort(seen.begin(), seen.end());
+    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return VRT_ERR_INVALID;
+    for (int i = 0; i < n_states; ++i)
+        if (st[i]->poisoned) return VRT_ERR_POISONED;
+    return VRT_OK;
+}
+
+std::vector<int> split_feed(int n, int max_batch) {
+    std::vector<int> out;
+    for (int t = 0; t < n; t += max_batch) out.push_back(std::min(max_batch, n - t));
+    return out;
+}
+
+// One kernel launch's worth of units: a list of states (by call index) and a
+// layer range relative to the call's layer0.  All layers of a state in one
+// launch share (abs_base, n_kv).
+struct Plan {
+    std::vector<int> states;
+    int l_off, nl;
+};
+
+// Group the call's units into launches.  A state whose layers all hold the
+// same (abs_base, n_kv) goes into an all-layer launch; a state whose layers
+// differ is launched layer by layer.
+std::vector<Plan> plan_launches(vrt_stream_state* const* st, int n_states, int layer0,
+                                int n_layers) {
+    std::vector<Plan> plans;
+    std::vector<int> uniform, ragged;
+    for (int i = 0; i < n_states; ++i) {
+        bool u = true;
+        for (int l = 1; l < n_layers && u; ++l)
+            u = st[i]->abs_base[layer0 + l] == st[i]->abs_base[layer0] &&
+                st[i]->n_kv[layer0 + l] == st[i]->n_kv[layer0];
+        (u ? uniform : ragged).push_back(i);
+    }
+    for (size_t b = 0; b < uniform.size(); b += kMaxStates) {
+        Plan p;
+        p.states.assign(uniform.begin() + b,
+                        uniform.begin() + std::min(uniform.size(), b + (size_t)kMaxStates));
+        p.l_off = 0;
+        p.nl = n_layers;
+        plans.push_back(p);
+    }
+    for (int l = 0; l < n_layers && !ragged.empty(); ++l)
+        for (size_t b = 0; b < ragged.size(); b += kMaxStates) {
+            Plan p;
+            p.states.assign(ragged.begin() + b,
+                            ragged.begin() + std::min(ragged.size(), b + (size_t)kMaxStates));
+            p.l_off = l;
+            p.nl = 1;
+            plans.push_back(p);
+        }
+    return plans;
+}
+
+void fill_table(const Plan& p, vrt_stream_state* const* st, int layer, StateTable* t) {
+    for (size_t i = 0; i < p.states.size(); ++i) {
+        const vrt_stream_state* s = st[p.states[i]];
+        t->ring[i] = (unsigned long long)(uintptr_t)s->dev;
+        t->p0[i] = s->abs_base[layer] + s->n_kv[layer];
+        t->n_kv[i] = s->n_kv[layer];
+        t->call_idx[i] = p.states[i];
+    }
+}
+
+void poison(vrt_stream_state* const* st, int n) {
+    for (int i = 0; i < n; ++i) st[i]->poisoned = true;
+}
+
+// Enqueue compaction of the given (state, layer) rings and advance their
+// mirrors.  `which` lists (call index, layer) pairs with n_kv > window.
+hipError_t run_compactions(vrt_stream_state* const* st,
+                           const std::vector<std::pair<int, int>>& which, hipStream_t stream) {
+    if (which.empty()) return hipSuccess;
+    const vrt_cache_desc& d = st[which[0].first]->d;
+    CompactArgs a;
+    a.g = make_geom(d);
+    a.kept = d.window;
+    CompactTable t;
+    for (size_t b = 0; b < which.size(); b += kMaxCompact) {
+        const size_t e = std::min(which.size(), b + (size_t)kMaxCompact);
+        a.n_entries = (int)(e - b);
+        for (size_t i = b; i < e; ++i) {
+            vrt_stream_state* s = st[which[i].first];
+            const int l = which[i].second;
+            t.layer_ring[i - b] =
+                (unsigned long long)(uintptr_t)(s->dev + (size_t)l * layer_bytes(d));
+            t.shift[i - b] = s->n_kv[l] - d.window;
+        }
+        const hipError_t err = note(launch_compact(a, t, stream));
+        if (err != hipSuccess) return err;
+    }
+    for (const auto& w : which) {
+        vrt_stream_state* s = st[w.first];
+        const int l = w.second;
+        s->abs_base[l] += s->n_kv[l] - d.window;
+        s->n_kv[l] = d.window;
+    }
+    return hipSuccess;
+}
+
+UnitMap make_map(const Plan& p, int layer0, int n_layers, int n_total, int t0, int n) {
+    UnitMap m;
+    m.n_states = (int)p.states.size();
+    m.nl = p.nl;
+    m.l_off = p.l_off;
+    m.nl_call = n_layers;
+    m.layer0 = layer0;
+    m.n_total = n_total;
+    m.t0 = t0;
+    m.n = n;
+    return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vrt_status_str(vrt_status s) {
+    switch (s) {
+        case VRT_OK: return "ok";
+        case VRT_ERR_INVALID: return "invalid argument";
+        case VRT_ERR_UNSUPPORTED: return "unsupported configuration";
+        case VRT_ERR_CAPACITY: return "insufficient capacity";
+        case VRT_ERR_DEVICE: return "device error";
+        case VRT_ERR_POISONED: return "state poisoned by an earlier device error";
+    }
+    return "unknown status";
+}
+
+const char* vrt_version(void) { return "vrt 0.1 gfx950"; }
+
+const char* vrt_last_device_error(void) { return g_last_error; }
+
+vrt_status vrt_desc_check(const vrt_cache_desc* desc) { return check_desc(desc); }
+
+size_t vrt_state_device_bytes(const vrt_cache_desc* desc) {
+    if (check_desc(desc) != VRT_OK) return 0;
+    return (size_t)desc->n_layers * layer_bytes(*desc);
+}
+
+size_t vrt_ring_offset(const vrt_cache_desc* desc, int layer, int which, int kv_head) {
+    if (check_desc(desc) != VRT_OK || layer < 0 || layer >= desc->n_layers || which < 0 ||
+        which > 1 || kv_head < 0 || kv_head >= desc->n_heads_kv)
+        return (size_t)-1;
+    return (size_t)layer * layer_bytes(*desc) +
+           ((size_t)which * desc->n_heads_kv + kv_head) * slice_bytes(*desc);
+}
+
+vrt_status vrt_stream_state_create(const vrt_cache_desc* desc, void* dev_mem, size_t bytes,
+                                   int64_t start_pos, vrt_stream_state** out) {
+    const vrt_status s = check_desc(desc);
+    if (s != VRT_OK) return s;
+    if (!out || !dev_mem || ((uintptr_t)dev_mem & 255) != 0) return VRT_ERR_INVALID;
+    if (start_pos < 0 || start_pos >= kPosLimit) return VRT_ERR_INVALID;
+    if (bytes < vrt_state_device_bytes(desc)) return VRT_ERR_CAPACITY;
+    vrt_stream_state* st = new (std::nothrow) vrt_stream_state;
+    if (!st) return VRT_ERR_CAPACITY;
+    st->d = *desc;
+    st->dev = (char*)dev_mem;
+    st->bytes = bytes;
+    st->abs_base.assign(desc->n_layers, start_pos);
+    st->n_kv.assign(desc->n_layers, 0);
+    st->poisoned = false;
+    *out = st;
+    return VRT_OK;
+}
+
+vrt_status vrt_stream_state_reset(vrt_stream_state* st, int64_t start_pos) {
+    if (!st || start_pos < 0 || start_pos >= kPosLimit) return VRT_ERR_INVALID;
+    std::fill(st->abs_base.begin(), st->abs_base.end(), start_pos);
+    std::fill(st->n_kv.begin(), st->n_kv.end(), 0);
+    st->poisoned = false;
+    return VRT_OK;
+}
+
+void vrt_stream_state_destroy(vrt_stream_state* st) { delete st; }
+
+vrt_status vrt_stream_state_query(const vrt_stream_state* st, int layer, int64_t* abs_base,
+                                  int32_t* n_kv) {
+    if (!st || layer < 0 || layer >= st->d.n_layers) return VRT_ERR_INVALID;
+    if (abs_base) *abs_base = st->abs_base[layer];
+    if (n_kv) *n_kv = st->n_kv[layer];
+    return st->poisoned ? VRT_ERR_POISONED : VRT_OK;
+}
+
+vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32_t* n_kv,
+                            int n_new, int32_t* n_compactions) {
+    const vrt_status s = check_desc(desc);
+    if (s != VRT_OK) return s;
+    if (desc->kind != VRT_ENC_RING || !abs_base || !n_kv || n_new < 0) return VRT_ERR_INVALID;
+    if (*n_kv < 0 || *n_kv > desc->ring_slots) return VRT_ERR_INVALID;
+    int64_t base = *abs_base;
+    int32_t nkv = *n_kv, nc = 0;
+    for (int m : split_feed(n_new, desc->max_batch)) {
+        if (nkv + m > desc->ring_slots) {
+            base += nkv - desc->window;
+            nkv = desc->window;
+            ++nc;
+        }
+        nkv += m;
+    }
+    *abs_base = base;
+    *n_kv = nkv;
+    if (n_compactions) *n_compactions = nc;
+    return VRT_OK;
+}
+
+int vrt_attn_path(const vrt_cache_desc* desc, int n) {
+    (void)desc;
+    (void)n;
+    return 0;
+}
+
+size_t vrt_offline_scratch_bytes(const vrt_cache_desc* desc, int T) {
+    if (check_desc(desc) != VRT_OK || T < 1) return 0;
+    return 2 * (size_t)desc->n_heads_kv * (size_t)T * desc->head_dim * elem_bytes(*desc);
+}
+
+vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const void* k,
+                                const void* v, int T, int64_t start_pos, void* out,
+                                void* scratch, size_t scratch_bytes, hipStream_t stream) {
+    const vrt_status s = check_desc(desc);
+    if (s != VRT_OK) return s;
+    if (desc->kind != VRT_ENC_RING) return VRT_ERR_INVALID;
+    if (!q || !k || !v || !out || !scratch || T < 1) return VRT_ERR_INVALID;
+    if (start_pos < 0 || start_pos > kPosLimit - T) return VRT_ERR_INVALID;
+    if (scratch_bytes < vrt_offline_scratch_bytes(desc, T)) return VRT_ERR_CAPACITY;
+
+    // The whole sequence is one linear "ring" of T slots in the scratch.
+    Geom g = make_geom(*desc);
+    g.slots = T;
+    g.mod = 0;
+    g.slice_bytes = (long long)T * desc->head_dim * elem_bytes(*desc);
+    g.v_off = (long long)desc->n_heads_kv * g.slice_bytes;
+    g.layer_bytes = 2 * g.v_off;
+    StateTable t;
+    t.ring[0] = (unsigned long long)(uintptr_t)scratch;
+    t.p0[0] = start_pos;
+    t.n_kv[0] = 0;
+    t.call_idx[0] = 0;
+    Plan p;
+    p.states = {0};
+    p.l_off = 0;
+    p.nl = 1;
+    const UnitMap m = make_map(p, 0, 1, T, 0, T);
+
+    AppendArgs aa;
+    aa.g = g;
+    aa.m = m;
+    aa.k = k;
+    aa.v = v;
+    clear_sticky_error();
+    if (note(launch_rope_append(aa, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+
+    AttnArgs at;
+    at.g = g;
+    at.m = m;
+    at.q = q;
+    at.k = k;
+    at.v = v;
+    at.out = out;
+    at.partials = nullptr;
+    at.qchunk = kRows / g.group;
+    at.n_qchunks = (T + at.qchunk - 1) / at.qchunk;
+    at.n_splits = 1;
+    at.split_len = kSplitLen;
+    at.scale_log2 = scale_log2(desc->head_dim);
+    at.append = 0;
+    if (note(launch_attn_valu(at, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    return VRT_OK;
+}
+
+vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int layer0,
+                             int n_layers, const void* q, const void* k, const void* v,
+                             int n_new, void* out, hipStream_t stream) {
+    vrt_status s = check_batch(st, n_states, layer0, n_layers, VRT_ENC_RING);
+    if (s != VRT_OK) return s;
+    if (!q || !k || !v || !out || n_new < 1) return VRT_ERR_INVALID;
+    for (int i = 0; i < n_states; ++i)
+        for (int l = layer0; l < layer0 + n_layers; ++l)
+            if (st[i]->abs_base[l] + st[i]->n_kv[l] > kPosLimit - n_new) return VRT_ERR_INVALID;
+
+    const vrt_cache_desc& d = st[0]->d;
+    const Geom g = make_geom(d);
+    clear_sticky_error();
+    int t0 = 0;
+    for (int m : split_feed(n_new, d.max_batch)) {
+        std::vector<std::pair<int, int>> comp;
+        for (int i = 0; i < n_states; ++i)
+            for (int l = layer0; l < layer0 + n_layers; ++l)
+                if (st[i]->n_kv[l] + m > d.ring_slots) comp.emplace_back(i, l);
+        if (run_compactions(st, comp, stream) != hipSuccess) {
+            poison(st, n_states);
+            return VRT_ERR_DEVICE;
+        }
+        for (const Plan& p : plan_launches(st, n_states, layer0, n_layers)) {
+            StateTable t;
+            fill_table(p, st, layer0 + p.l_off, &t);
+            const UnitMap um = make_map(p, layer0, n_layers, n_new, t0, m);
+            AppendArgs aa;
+            aa.g = g;
+            aa.m = um;
+            aa.k = k;
+            aa.v = v;
+            AttnArgs at;
+            at.g = g;
+            at.m = um;
+            at.q = q;
+            at.k = k;
+            at.v = v;
+            at.out = out;
+            at.partials = nullptr;
+            at.qchunk = kRows / g.group;
+            at.n_qchunks = (m + at.qchunk - 1) / at.qchunk;
+            at.n_splits = 1;
+            at.split_len = kSplitLen;
+            at.scale_log2 = scale_log2(d.head_dim);
+            // one query chunk per unit: the attention launch appends the
+            // new rows itself; otherwise a separate append launch runs first
+            at.append = at.n_qchunks == 1 ? 1 : 0;
+            if ((!at.append && note(launch_rope_append(aa, t, stream)) != hipSuccess) ||
+                note(launch_attn_valu(at, t, stream)) != hipSuccess) {
+                poison(st, n_states);
+                return VRT_ERR_DEVICE;
+            }
+        }
+        for (int i = 0; i < n_states; ++i)
+            for (int l = layer0; l < layer0 + n_layers; ++l) st[i]->n_kv[l] += m;
+        t0 += m;
+    }
+    return VRT_OK;
+}
+
+vrt_status vrt_ring_compact(vrt_stream_state* const* st, int n_states, int layer0, int n_layers,
+                            hipStream_t stream) {
+    const vrt_status s = check_batch(st, n_states, layer0, n_layers, VRT_ENC_RING);
+    if (s != VRT_OK) return s;
+    std::vector<std::pair<int, int>> comp;
+    for (int i = 0; i < n_states; ++i)
+        for (int l = layer0; l < layer0 + n_layers; ++l)
+            if (st[i]->n_kv[l] > st[i]->d.window) comp.emplace_back(i, l);
+    clear_sticky_error();
+    if (run_compactions(st, comp, stream) != hipSuccess) {
+        poison(st, n_states);
+        return VRT_ERR_DEVICE;
+    }
+    return VRT_OK;
+}
+
+size_t vrt_dec_workspace_bytes(const vrt_cache_desc* desc, int n_states, int n_layers,
+                               int n_tok) {
+    if (check_desc(desc) != VRT_OK || n_states < 1 || n_layers < 1 || n_tok < 1) return 0;
+    if (n_tok > 1) return 0;  // prefill needs no workspace
+    const size_t n_splits = (size_t)(desc->window + kSplitLen - 2) / kSplitLen + 1;
+    const size_t group = desc->n_heads_q / desc->n_heads_kv;
+    return (size_t)n_states * n_layers * desc->n_heads_kv * n_splits * group *
+           (2 + desc->head_dim) * sizeof(float);
+}
+
+vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int layer0,
+                             int n_layers, const void* q, const void* k, const void* v,
+                             int n_tok, void* out, void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+    vrt_status s = check_batch(st, n_states, layer0, n_layers, VRT_DEC_MODRING);
+    if (s != VRT_OK) return s;
+    if (!q || !k || !v || !out || n_tok < 1) return VRT_ERR_INVALID;
+    const vrt_cache_desc& d = st[0]->d;
+    if (n_tok == 1) {
+        if (!workspace) return VRT_ERR_INVALID;
+        if (ws_bytes < vrt_dec_workspace_bytes(&d, n_states, n_layers, 1)) return VRT_ERR_CAPACITY;
+    }
+    // positions in range, and no sub-batch of a prefill overwrites a slot that
+    // one of its own queries still reads
+    const std::vector<int> subs = split_feed(n_tok, d.max_batch);
+    for (int i = 0; i < n_states; ++i)
+        for (int l = layer0; l < layer0 + n_layers; ++l) {
+            const int64_t start = st[i]->abs_base[l];
+            int64_t next = start + st[i]->n_kv[l];
+            if (next > kPosLimit - n_tok || (int64_t)st[i]->n_kv[l] + n_tok > INT_MAX)
+                return VRT_ERR_INVALID;
+            for (int m : subs) {
+                const int64_t evicted_max = next + m - 1 - d.ring_slots;
+                const int64_t needed_min = std::max(start, next - d.window + 1);
+                if (m > 1 && evicted_max >= needed_min) return VRT_ERR_INVALID;
+                next += m;
+            }
+        }
+
+    const Geom g = make_geom(d);
+    const int n_splits = (d.window + kSplitLen - 2) / kSplitLen + 1;
+    clear_sticky_error();
+    int t0 = 0;
+    for (int m : subs) {
+        for (const Plan& p : plan_launches(st, n_states, layer0, n_layers)) {
+            StateTable t;
+            fill_table(p, st, layer0 + p.l_off, &t);
+            const UnitMap um = make_map(p, layer0, n_layers, n_tok, t0, m);
+            AppendArgs aa;
+            aa.g = g;
+            aa.m = um;
+            aa.k = k;
+            aa.v = v;
+            AttnArgs at;
+            at.g = g;
+            at.m = um;
+            at.q = q;
+            at.k = k;
+            at.v = v;
+            at.out = out;
+            at.split_len = kSplitLen;
+            at.scale_log2 = scale_log2(d.head_dim);
+            if (m == 1) {
+                at.partials = (float*)workspace;
+                at.qchunk = 1;
+                at.n_qchunks = 1;
+                at.n_splits = n_splits;
+            } else {
+                at.partials = nullptr;
+                at.qchunk = kRows / g.group;
+                at.n_qchunks = (m + at.qchunk - 1) / at.qchunk;
+                at.n_splits = 1;
+            }
+            at.append = at.n_qchunks == 1 ? 1 : 0;
+            hipError_t err = hipSuccess;
+            if (!at.append) err = note(launch_rope_append(aa, t, stream));
+            if (err == hipSuccess) err = note(launch_attn_valu(at, t, stream));
+            if (err == hipSuccess && m == 1) err = note(launch_dec_combine(at, t, stream));
+            if (err != hipSuccess) {
+                poison(st, n_states);
+                return VRT_ERR_DEVICE;
+            }
+        }
+        for (int i = 0; i < n_states; ++i)
+            for (int l = layer0; l < layer0 + n_layers; ++l) st[i]->n_kv[l] += m;
+        t0 += m;
+    }
+    return VRT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Internal launch interface between the C-ABI host code (vrt_host.cpp) and the
+// gfx950 kernels (vrt_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace vrt {
+
+// States per launch.  The per-state table travels in the kernel arguments
+// (no device-side table to upload, nothing for the library to allocate);
+// 128 entries keep the argument block near 3.2 KB.
+constexpr int kMaxStates = 128;
+// Compaction entries per launch (one entry = one (state, layer) ring).
+constexpr int kMaxCompact = 256;
+// Keys per tile; tiles start at multiples of 64 in absolute position.
+constexpr int kTile = 64;
+// Query rows (q head x position) handled by one VALU attention workgroup.
+constexpr int kRows = 16;
+// Keys per split of the decode step; splits start at multiples of this in
+// absolute position and are merged in ascending order.
+constexpr int kSplitLen = 1024;
+// Sentinel for "no key seen yet" in the running maximum (finite on purpose:
+// exp2(SENT - SENT) = 1 keeps fully masked tiles exact no-ops).
+constexpr float kSent = -1.0e30f;
+
+// Geometry of one cache kind, shared by every state of a launch.
+struct Geom {
+    int dtype;          // 0 f32, 1 bf16
+    int D;              // head_dim
+    int hq, hkv, group; // query heads, kv heads, hq / hkv
+    int slots;          // ring slots per (layer, kv head)
+    int window;         // W
+    int mod;            // 1: slot = pos % slots; 0: slot = pos - abs_base
+    long long layer_bytes;  // bytes per layer inside a state (K ring + V ring)
+    long long slice_bytes;  // bytes per kv-head slice = slots * D * elem
+    long long v_off;        // byte offset of the V ring inside a layer
+    double theta;           // RoPE base
+};
+
+// Per-state entries of one launch.  p0 = absolute position of the first new
+// frame of this sub-batch; n_kv = rows (tokens, for the decoder) the ring held
+// before this sub-batch was appended, so abs_base = p0 - n_kv.
+struct StateTable {
+    unsigned long long ring[kMaxStates];
+    long long p0[kMaxStates];
+    int n_kv[kMaxStates];
+    int call_idx[kMaxStates];   // index of the state within the call's arrays
+};
+
+// How a launch's units map to the call's input/output arrays.
+//   unit (si, li) of the launch  ->  call unit call_idx[si] * nl_call + l_off + li
+//   state layer index            ->  layer0 + l_off + li
+//   element offset of frame f    ->  (call_unit * n_total + t0 + f) * heads * D
+struct UnitMap {
+    int n_states;   // states in this launch (<= kMaxStates)
+    int nl;         // layers in this launch
+    int l_off;      // first layer of the launch, relative to the call's layer0
+    int nl_call;    // layers in the call
+    int layer0;     // state layer index of the call's first layer
+    int n_total;    // frames per unit in the caller's arrays (n_new / n_tok)
+    int t0;         // first frame of this sub-batch inside those arrays
+    int n;          // frames in this sub-batch
+};
+
+struct AppendArgs {
+    Geom g;
+    UnitMap m;
+    const void* k;
+    const void* v;
+};
+
+struct AttnArgs {
+    Geom g;
+    UnitMap m;
+    const void* q;
+    const void* k;      // new keys / values (fused append only)
+    const void* v;
+    void* out;          // [call unit][frame][hq][D]  (non-split)
+    float* partials;    // split mode: [call unit][hkv][split][group][2 + D]
+    int qchunk;         // positions per workgroup
+    int n_qchunks;
+    int n_splits;       // 1 = no split
+    int split_len;
+    float scale_log2;   // log2(e) / sqrt(D)
+    int append;         // 1: the attention launch also appends the new K/V rows
+};
+
+struct CompactTable {
+    unsigned long long layer_ring[kMaxCompact];  // base of the (state, layer) K ring
+    int shift[kMaxCompact];                      // rows dropped from the front
+};
+
+struct CompactArgs {
+    Geom g;
+    int n_entries;
+    int kept;           // rows kept (= window)
+};
+
+hipError_t launch_rope_append(const AppendArgs& a, const StateTable& t, hipStream_t s);
+hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t s);
+hipError_t launch_dec_combine(const AttnArgs& a, const StateTable& t, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, const CompactTable& t, hipStream_t s);
+
+}  // namespace vrt

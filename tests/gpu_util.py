@@ -1,0 +1,90 @@
+"""Helpers for the GPU parity tests: device upload/download, state pools and
+the error measures the parity bar is written in.
+
+Tolerances (written in the tests): fp32 storage, norm-wise relative error
+max|gpu - oracle| / max|oracle| <= 1e-5 per output tensor; bf16 storage,
+max-abs error <= 2e-2 (the relative figure is reported beside it)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import sliding_window_cached_amd as vrt
+
+DEV = torch.device("cuda:0")
+F32_TOL = 1e-5
+BF16_TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def to_dev(x: np.ndarray, dtype: int) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+    return t.to(torch.bfloat16) if dtype == vrt.BF16 else t
+
+
+def empty(shape, dtype: int) -> torch.Tensor:
+    return torch.empty(shape, dtype=torch.bfloat16 if dtype == vrt.BF16 else torch.float32,
+                       device=DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def rel_err(a, ref) -> float:
+    return float(np.abs(np.asarray(a, np.float64) - ref).max() / np.abs(ref).max())
+
+
+def abs_err(a, ref) -> float:
+    return float(np.abs(np.asarray(a, np.float64) - ref).max())
+
+
+def check_close(a, ref, dtype, what=""):
+    if dtype == vrt.F32:
+        e = rel_err(a, ref)
+        say(f"  {what}: fp32 rel err {e:.3e} (tol {F32_TOL:g})")
+        assert e <= F32_TOL, (what, e)
+    else:
+        e, r = abs_err(a, ref), rel_err(a, ref)
+        say(f"  {what}: bf16 max-abs err {e:.3e} (tol {BF16_TOL:g}), rel {r:.3e}")
+        assert e <= BF16_TOL, (what, e)
+
+
+class Pool:
+    """n states over one device allocation."""
+
+    def __init__(self, desc, n: int, starts):
+        self.desc = desc
+        self.nbytes = vrt.state_device_bytes(desc)
+        self.mem = torch.empty(n * self.nbytes, dtype=torch.uint8, device=DEV)
+        self.states = [vrt.StreamState(desc, self.mem[i * self.nbytes:(i + 1) * self.nbytes],
+                                       self.nbytes, int(starts[i])) for i in range(n)]
+
+    def ring_rows(self, i: int, layer: int, which: int, head: int, s0: int, s1: int) -> np.ndarray:
+        """Rows [s0, s1) of one ring slice, as float32 values."""
+        d = self.desc
+        e = 2 if d.dtype == vrt.BF16 else 4
+        off = i * self.nbytes + vrt.ring_offset(d, layer, which, head)
+        raw = self.mem[off + s0 * d.head_dim * e: off + s1 * d.head_dim * e]
+        t = raw.view(torch.bfloat16 if e == 2 else torch.float32)
+        return t.float().cpu().numpy().reshape(s1 - s0, d.head_dim)
+
+    def ring_bytes(self, i: int, layer: int, which: int, head: int, s0: int, s1: int) -> bytes:
+        d = self.desc
+        e = 2 if d.dtype == vrt.BF16 else 4
+        off = i * self.nbytes + vrt.ring_offset(d, layer, which, head)
+        return self.mem[off + s0 * d.head_dim * e: off + s1 * d.head_dim * e].cpu().numpy().tobytes()
+
+    def close(self):
+        for s in self.states:
+            s.close()

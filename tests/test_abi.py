@@ -1,0 +1,172 @@
+"""CPU tests of the C ABI: the library loads and exports every symbol the
+public header declares, descriptors are checked as documented, the host ring
+planner agrees with the oracle's ring model, and argument errors are caught
+before anything is enqueued.  No compute call is made here (no GPU)."""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import sliding_window_cached_amd as vrt
+from oracle.ring import EncRing
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vrt.h")
+
+
+def test_exports_every_declared_symbol():
+    text = open(HDR).read()
+    declared = set(re.findall(r"\b(vrt_[a-z_0-9]+)\s*\(", text))
+    assert len(declared) >= 17
+    lib = ctypes.CDLL(vrt.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert declared == set(vrt.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in vrt.version()
+    for s in range(6):
+        assert vrt.status_str(s)
+
+
+def test_desc_checks():
+    assert vrt.desc_check(vrt.enc_desc()) == vrt.OK
+    assert vrt.desc_check(vrt.dec_desc()) == vrt.OK
+    assert vrt.desc_check(vrt.enc_desc(head_dim=96)) == vrt.ERR_UNSUPPORTED
+    assert vrt.desc_check(vrt.enc_desc(ring_slots=1261)) == vrt.ERR_UNSUPPORTED  # < W + max_batch
+    assert vrt.desc_check(vrt.enc_desc(ring_slots=1262)) == vrt.OK
+    assert vrt.desc_check(vrt.dec_desc(ring_slots=8000)) == vrt.ERR_UNSUPPORTED  # < window
+    assert vrt.desc_check(vrt.dec_desc(ring_slots=8200)) == vrt.ERR_UNSUPPORTED  # not 64-multiple
+    assert vrt.desc_check(vrt.dec_desc(ring_slots=16384)) == vrt.OK
+    d = vrt.enc_desc()
+    d.reserved = 1
+    assert vrt.desc_check(d) == vrt.ERR_INVALID
+    assert vrt.desc_check(vrt.enc_desc(heads=0)) == vrt.ERR_INVALID
+    assert vrt.desc_check(vrt.dec_desc(heads_q=30)) == vrt.ERR_INVALID  # not a multiple of 8
+    assert vrt.desc_check(vrt.dec_desc(heads_q=256, heads_kv=8)) == vrt.ERR_UNSUPPORTED  # group 32
+    bad = vrt.enc_desc()
+    bad.dtype = 7
+    assert vrt.desc_check(bad) == vrt.ERR_UNSUPPORTED
+
+
+def test_state_bytes_and_offsets():
+    d = vrt.enc_desc(n_layers=32)
+    assert vrt.state_device_bytes(d) == 32 * 2 * 20 * 1536 * 64 * 2
+    dd = vrt.dec_desc(n_layers=26)
+    assert vrt.state_device_bytes(dd) == 26 * 2 * 8 * 8192 * 128 * 2
+    sl = 1536 * 64 * 2
+    assert vrt.ring_offset(d, 0, 0, 0) == 0
+    assert vrt.ring_offset(d, 0, 1, 0) == 20 * sl
+    assert vrt.ring_offset(d, 3, 1, 5) == 3 * 40 * sl + 25 * sl
+    assert vrt.ring_offset(d, 32, 0, 0) == 2 ** 64 - 1
+    assert vrt.offline_scratch_bytes(d, 1000) == 2 * 20 * 1000 * 64 * 2
+
+
+def test_ring_advance_matches_oracle_model():
+    d = vrt.enc_desc()
+    rng = random.Random(0)
+    for trial in range(200):
+        r = EncRing()
+        start = rng.randrange(0, 10 ** 6)
+        r.reset(start)
+        base, nkv = start, 0
+        for _ in range(rng.randrange(1, 40)):
+            n = rng.choice([1, 2, 3, 4, 7, 31, 32, 100, 511, 512, 513, 750, 1536, 2000])
+            before = len(r.events)
+            r.feed(n)
+            base, nkv, nc = vrt.ring_advance(d, base, nkv, n)
+            assert (base, nkv) == (r.abs_base, r.n_kv)
+            assert nc == len(r.events) - before
+
+
+def test_attn_path_is_a_function_of_dtype_and_n():
+    f32, bf = vrt.enc_desc(dtype=vrt.F32), vrt.enc_desc(dtype=vrt.BF16)
+    for n in (1, 4, 16, 31, 32, 512):
+        assert vrt.attn_path(f32, n) == 0
+        assert vrt.attn_path(bf, n) in (0, 1)
+    assert vrt.attn_path(bf, 4) == 0
+
+
+# A 256-byte aligned fake address: valid for host bookkeeping, never touched,
+# because every call below fails its argument checks before enqueueing.
+FAKE = 1 << 40
+
+
+def _state(desc, start=0):
+    return vrt.StreamState(desc, FAKE, vrt.state_device_bytes(desc), start)
+
+
+def test_create_reset_query_host_only():
+    d = vrt.enc_desc(n_layers=3)
+    st = _state(d, 42)
+    assert st.query(0) == (42, 0) and st.query(2) == (42, 0)
+    st.reset(7)
+    assert st.query(1) == (7, 0)
+    with pytest.raises(vrt.VrtError) as e:
+        st.query(3)
+    assert e.value.status == vrt.ERR_INVALID
+    with pytest.raises(vrt.VrtError) as e:
+        vrt.StreamState(d, FAKE, vrt.state_device_bytes(d) - 1, 0)
+    assert e.value.status == vrt.ERR_CAPACITY
+    with pytest.raises(vrt.VrtError) as e:
+        vrt.StreamState(d, FAKE + 8, vrt.state_device_bytes(d), 0)   # misaligned
+    assert e.value.status == vrt.ERR_INVALID
+    with pytest.raises(vrt.VrtError) as e:
+        vrt.StreamState(d, FAKE, vrt.state_device_bytes(d), -1)
+    assert e.value.status == vrt.ERR_INVALID
+
+
+def test_feed_argument_errors_enqueue_nothing():
+    d = vrt.enc_desc(n_layers=2)
+    a, b = _state(d), _state(d)
+    other = _state(vrt.enc_desc(n_layers=3))
+    dec = _state(vrt.dec_desc(n_layers=2))
+    P = FAKE
+    cases = [
+        ([a], 0, 1, None, 4),        # null q
+        ([a], 0, 1, P, 0),           # n_new = 0
+        ([a], 1, 2, P, 4),           # layer range past n_layers
+        ([a], -1, 1, P, 4),
+        ([a, a], 0, 1, P, 4),        # repeated state
+        ([a, other], 0, 1, P, 4),    # mixed descs
+        ([dec], 0, 1, P, 4),         # decoder state into the encoder feed
+    ]
+    for states, l0, nl, q, n in cases:
+        s = vrt.enc_attn_feed(states, l0, nl, q, P, P, n, P, 0, check=False)
+        assert s == vrt.ERR_INVALID, (l0, nl, q, n)
+    for st in (a, b):
+        assert st.query(0) == (0, 0) and st.query(1) == (0, 0)
+    with pytest.raises(vrt.VrtError):
+        vrt.ring_compact([dec], 0, 1)
+
+
+def test_decoder_argument_errors():
+    d = vrt.dec_desc(n_layers=1, window=256, ring_slots=256)
+    st = _state(d)
+    P = FAKE
+    ws = vrt.dec_workspace_bytes(d, 1, 1, 1)
+    assert ws > 0
+    # missing workspace for a decode step
+    assert vrt.dec_attn_step([st], 0, 1, P, P, P, 1, P, None, 0, check=False) == vrt.ERR_INVALID
+    assert vrt.dec_attn_step([st], 0, 1, P, P, P, 1, P, P, ws - 4, check=False) == vrt.ERR_CAPACITY
+    # a 300-token prefill on a 256-slot ring would overwrite keys its own
+    # first queries need
+    assert vrt.dec_attn_step([st], 0, 1, P, P, P, 300, P, check=False) == vrt.ERR_INVALID
+    assert st.query(0) == (0, 0)
+
+
+def test_single_hip_runtime_in_process():
+    """libvrt and PyTorch must share one HIP runtime (a second runtime in the
+    same process sees no GPU), whichever is imported first."""
+    import subprocess
+    import sys
+    code = ("import sliding_window_cached_amd, torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "paths = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+            "print(len(paths)); print(sorted(paths))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split("\n")[0] == "1", r.stdout

@@ -108,3 +108,12 @@ def test_position_shift_invariance():
     a = attention.windowed(q, k, v, 0, 9, THETA)
     b = attention.windowed(q, k, v, 987_654, 9, THETA)
     assert np.max(np.abs(a - b)) <= 1e-9
+
+
+def test_sampled_rows_equal_whole_sequence():
+    T, W = 50, 7
+    q, k, v = _rand(11, T, 4, 2, 8)
+    full = attention.windowed(q, k, v, 300, W, THETA)
+    ts = [0, 1, 6, 7, 30, 49]
+    part = attention.windowed_at(q, k, v, 300, W, THETA, ts)
+    assert np.array_equal(part, full[ts])
