@@ -177,8 +177,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=["c2"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-streams", type=int, default=2)
-    ap.add_argument("--cpu-steps", type=int, default=600)
+    ap.add_argument("--cpu-streams", type=int, default=1)
+    ap.add_argument("--cpu-steps", type=int, default=400)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: streams are independent and would shard across "

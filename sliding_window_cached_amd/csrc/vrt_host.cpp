@@ -94,11 +94,34 @@ Geom make_geom(const vrt_cache_desc& d) {
     g.slice_bytes = (long long)slice_bytes(d);
     g.v_off = (long long)d.n_heads_kv * g.slice_bytes;
     g.layer_bytes = 2 * g.v_off;
-    g.theta = d.rope_theta;
+    for (int i = 0; i < 64; ++i)
+        g.omega[i] = i < d.head_dim / 2 ? std::pow(d.rope_theta, -2.0 * i / d.head_dim) : 0.0;
     return g;
 }
 
 float scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
+
+// kv heads per attention workgroup: the largest divisor of hkv whose rotated
+// query rows fit the workgroup's LDS budget and that still leaves about four
+// workgroups per compute unit, so each workgroup streams a long run of tiles
+// through one pipeline.
+int pick_hg(const Geom& g, long long units, int rows_per_head, long long qchunks, long long splits) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    const long long target = 4LL * cus;
+    const int elem = g.dtype == 1 ? 2 : 4;
+    int best = 1;
+    for (int h = 2; h <= g.hkv; ++h) {
+        if (g.hkv % h) continue;
+        if ((long long)h * rows_per_head * g.D * elem > kQsBytes) break;
+        if (units * (g.hkv / h) * qchunks * splits < target) break;
+        best = h;
+    }
+    return best;
+}
 
 // Common checks for the batched calls.  Pure: touches nothing.
 vrt_status check_batch(vrt_stream_state* const* st, int n_states, int layer0, int n_layers,
@@ -383,6 +406,7 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
     at.split_len = kSplitLen;
     at.scale_log2 = scale_log2(desc->head_dim);
     at.append = 0;
+    at.hg = pick_hg(g, 1, std::min(at.qchunk, T) * g.group, at.n_qchunks, 1);
     if (note(launch_attn_valu(at, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
     return VRT_OK;
 }
@@ -435,6 +459,8 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
             // one query chunk per unit: the attention launch appends the
             // new rows itself; otherwise a separate append launch runs first
             at.append = at.n_qchunks == 1 ? 1 : 0;
+            at.hg = pick_hg(g, (long long)um.n_states * um.nl, std::min(at.qchunk, m) * g.group,
+                            at.n_qchunks, 1);
             if ((!at.append && note(launch_rope_append(aa, t, stream)) != hipSuccess) ||
                 note(launch_attn_valu(at, t, stream)) != hipSuccess) {
                 poison(st, n_states);
@@ -538,6 +564,8 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int laye
                 at.n_splits = 1;
             }
             at.append = at.n_qchunks == 1 ? 1 : 0;
+            at.hg = pick_hg(g, (long long)um.n_states * um.nl, std::min(at.qchunk, m) * g.group,
+                            at.n_qchunks, at.n_splits);
             hipError_t err = hipSuccess;
             if (!at.append) err = note(launch_rope_append(aa, t, stream));
             if (err == hipSuccess) err = note(launch_attn_valu(at, t, stream));

@@ -9,14 +9,17 @@ namespace vrt {
 
 // States per launch.  The per-state table travels in the kernel arguments
 // (no device-side table to upload, nothing for the library to allocate);
-// 128 entries keep the argument block near 3.2 KB.
-constexpr int kMaxStates = 128;
+// 256 entries (one launch for 256 streams) make a 6 KB argument block;
+// kernel arguments of this size are passed intact on gfx950.
+constexpr int kMaxStates = 256;
 // Compaction entries per launch (one entry = one (state, layer) ring).
 constexpr int kMaxCompact = 256;
 // Keys per tile; tiles start at multiples of 64 in absolute position.
 constexpr int kTile = 64;
-// Query rows (q head x position) handled by one VALU attention workgroup.
+// Query rows (q head x position) of one kv head in one attention workgroup.
 constexpr int kRows = 16;
+// LDS bytes for the rotated query rows of a workgroup's kv-head group.
+constexpr int kQsBytes = 6144;
 // Keys per split of the decode step; splits start at multiples of this in
 // absolute position and are merged in ascending order.
 constexpr int kSplitLen = 1024;
@@ -35,7 +38,7 @@ struct Geom {
     long long layer_bytes;  // bytes per layer inside a state (K ring + V ring)
     long long slice_bytes;  // bytes per kv-head slice = slots * D * elem
     long long v_off;        // byte offset of the V ring inside a layer
-    double theta;           // RoPE base
+    double omega[64];       // RoPE frequencies theta^(-2i/D), i < D/2, fp64
 };
 
 // Per-state entries of one launch.  p0 = absolute position of the first new
@@ -84,6 +87,7 @@ struct AttnArgs {
     int split_len;
     float scale_log2;   // log2(e) / sqrt(D)
     int append;         // 1: the attention launch also appends the new K/V rows
+    int hg;             // kv heads per workgroup (divides hkv)
 };
 
 struct CompactTable {

@@ -28,6 +28,8 @@
 // keeps everything in fp32.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "vrt_internal.h"
 
 namespace vrt {
@@ -37,6 +39,29 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 struct F32T { static constexpr int E = 4; };
 struct BF16T { static constexpr int E = 2; };
+
+// Global-memory accesses go through address-space-1 pointers: the ring and
+// I/O addresses arrive as integers in the kernel arguments, and through a
+// generic pointer the compiler would emit flat loads, which also count on the
+// LDS wait counter and so make every LDS wait in the tile loop wait for the
+// next tiles' HBM loads too.
+#define VRT_GLOBAL __attribute__((address_space(1)))
+template <int B> struct Raw;
+template <> struct Raw<2> { typedef unsigned short T; };
+template <> struct Raw<4> { typedef unsigned int T; };
+template <> struct Raw<8> { typedef unsigned int T __attribute__((ext_vector_type(2))); };
+template <> struct Raw<16> { typedef unsigned int T __attribute__((ext_vector_type(4))); };
+template <class T>
+__device__ __forceinline__ T gld(const void* p) {
+    typedef typename Raw<sizeof(T)>::T R;
+    const R r = *(const VRT_GLOBAL R*)(__UINTPTR_TYPE__)p;
+    return __builtin_bit_cast(T, r);
+}
+template <class T>
+__device__ __forceinline__ void gst(void* p, T v) {
+    typedef typename Raw<sizeof(T)>::T R;
+    *(VRT_GLOBAL R*)(__UINTPTR_TYPE__)p = __builtin_bit_cast(R, v);
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -62,12 +87,10 @@ __device__ __forceinline__ long long floor_div(long long a, long long b) {
 }
 
 // ---------------------------------------------------------------- RoPE ----
-// omega_i = theta^(-2i/D); angle = pos * omega_i, both in fp64 (a float32
-// angle is off by up to ~0.03 rad at positions near 1e6).
-__device__ __forceinline__ void rope_angle(long long pos, int i, int D, double theta,
-                                           double* c, double* s) {
-    const double w = pow(theta, -2.0 * (double)i / (double)D);
-    sincos((double)pos * w, s, c);
+// angle = pos * omega_i in fp64 (a float32 angle is off by up to ~0.03 rad at
+// positions near 1e6); omega_i = theta^(-2i/D) comes from the host in fp64.
+__device__ __forceinline__ void rope_angle(long long pos, double omega, double* c, double* s) {
+    sincos((double)pos * omega, s, c);
 }
 
 // NEOX pair (i, i + D/2): y0 = x0 cos - x1 sin, y1 = x1 cos + x0 sin, in fp64,
@@ -84,22 +107,32 @@ __device__ __forceinline__ void rope_rot(float x0, float x1, double c, double s,
 
 template <class E> __device__ __forceinline__ void ld4(const char* p, float (&x)[4]);
 template <> __device__ __forceinline__ void ld4<F32T>(const char* p, float (&x)[4]) {
-    const float4 v = *(const float4*)p;
+    const float4 v = gld<float4>(p);
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
 }
 template <> __device__ __forceinline__ void ld4<BF16T>(const char* p, float (&x)[4]) {
-    const uint2 v = *(const uint2*)p;
+    const uint2 v = gld<uint2>(p);
     x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
 }
-template <class E> __device__ __forceinline__ void st4(char* p, const float (&x)[4]);
-template <> __device__ __forceinline__ void st4<F32T>(char* p, const float (&x)[4]) {
+// Four consecutive elements in the storage type; G: global memory, else LDS.
+template <class E, bool G> __device__ __forceinline__ void st4(char* p, const float (&x)[4]);
+template <> __device__ __forceinline__ void st4<F32T, true>(char* p, const float (&x)[4]) {
+    gst<float4>(p, make_float4(x[0], x[1], x[2], x[3]));
+}
+template <> __device__ __forceinline__ void st4<F32T, false>(char* p, const float (&x)[4]) {
     *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
 }
-template <> __device__ __forceinline__ void st4<BF16T>(char* p, const float (&x)[4]) {
+__device__ __forceinline__ uint2 pack_bf16x4(const float (&x)[4]) {
     uint2 v;
     v.x = to_bf16(x[0]) | (to_bf16(x[1]) << 16);
     v.y = to_bf16(x[2]) | (to_bf16(x[3]) << 16);
-    *(uint2*)p = v;
+    return v;
+}
+template <> __device__ __forceinline__ void st4<BF16T, true>(char* p, const float (&x)[4]) {
+    gst<uint2>(p, pack_bf16x4(x));
+}
+template <> __device__ __forceinline__ void st4<BF16T, false>(char* p, const float (&x)[4]) {
+    *(uint2*)p = pack_bf16x4(x);
 }
 
 // ---------------------------------------------------------- K1: append ----
@@ -120,7 +153,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
     for (int x = threadIdx.x; x < nf * H2; x += blockDim.x) {
         const int f = x / H2, i = x - f * H2;
         double c, s;
-        rope_angle(p0 + f0 + f, i, D, a.g.theta, &c, &s);
+        rope_angle(p0 + f0 + f, a.g.omega[i], &c, &s);
         cs[2 * x] = c;
         cs[2 * x + 1] = s;
     }
@@ -146,17 +179,17 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
             rope_rot(x0[q], x1[q], an[0], an[1], &y0[q], &y1[q]);
         }
         char* dst = layer + (long long)h * a.g.slice_bytes + slot * (D * E::E);
-        st4<E>(dst + 4 * c * E::E, y0);
-        st4<E>(dst + (H2 + 4 * c) * E::E, y1);
+        st4<E, true>(dst + 4 * c * E::E, y0);
+        st4<E, true>(dst + (H2 + 4 * c) * E::E, y1);
     }
     for (int x = threadIdx.x; x < nf * hkv * VCH; x += blockDim.x) {
         const int c = x % VCH, fh = x / VCH, h = fh % hkv, f = fh / hkv;
         const long long pos = p0 + f0 + f;
         const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + f0 + f);
         const uint4 val =
-            *(const uint4*)(vin + ((long long)f * row_elems + (long long)h * D) * E::E + 16 * c);
-        *(uint4*)(layer + a.g.v_off + (long long)h * a.g.slice_bytes + slot * (D * E::E) +
-                  16 * c) = val;
+            gld<uint4>(vin + ((long long)f * row_elems + (long long)h * D) * E::E + 16 * c);
+        gst<uint4>(layer + a.g.v_off + (long long)h * a.g.slice_bytes + slot * (D * E::E) + 16 * c,
+                   val);
     }
 }
 
@@ -181,76 +214,140 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a, CompactTable t) 
         const int nr = min(CHUNK, a.kept - r0);
         const int n16 = nr * ROWB / 16;
         for (int x = threadIdx.x; x < n16; x += blockDim.x)
-            stage[x] = *(const uint4*)(src + (long long)r0 * ROWB + 16LL * x);
+            stage[x] = gld<uint4>(src + (long long)r0 * ROWB + 16LL * x);
         __syncthreads();
         for (int x = threadIdx.x; x < n16; x += blockDim.x)
-            *(uint4*)(base + (long long)r0 * ROWB + 16LL * x) = stage[x];
+            gst<uint4>(base + (long long)r0 * ROWB + 16LL * x, stage[x]);
         __syncthreads();
     }
 }
 
-// ------------------------------------------------------ K3: attention ----
-template <class E, int D>
-struct Lds {
-    static constexpr int ROWDW = D * E::E / 4;           // dwords per K / q row
-    static constexpr int KP = ROWDW + 4;                 // padded K row pitch
-    static constexpr int VP = kTile * E::E / 4 + 4;      // padded V^T row pitch
-    static constexpr int KDW = kTile * KP;
-    static constexpr int VDW = D * VP;
-    static constexpr int BUF = KDW + VDW;
-    static constexpr int QDW = kRows * ROWDW;
-    static constexpr int PDW = kTile * E::E / 4;         // one P row per wave
-    static constexpr int TOTAL = 2 * BUF + QDW + 4 * PDW;
-    static constexpr int CPR = D * E::E / 16;            // 16-byte chunks per row
-    static constexpr int IPT = 32 * CPR / 256;           // (row pair, chunk) items per thread
-};
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Wave-wide reductions: xor-butterfly inside each row of 16 lanes with DPP
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror; with
+// every quad / half-row already holding one value the mirrors act as xor 4 /
+// xor 8), then the four row results combined as (r0 + r1) + (r2 + r3) from
+// readlane.  Each step combines the same two values on both partner lanes,
+// so every lane ends with bit-identical results.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
     return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v = v + dpp<0xB1>(v);
+    v = v + dpp<0x4E>(v);
+    v = v + dpp<0x141>(v);
+    v = v + dpp<0x140>(v);
+    return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = row_max16(v);
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = v + __shfl_xor(v, o);
-    return v;
+    v = row_sum16(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
-// One workgroup (4 waves) per (unit, kv head, query chunk, key split).  Rows
-// are (query position j, q head of the kv group): r = j * group + gh.  Wave w
-// owns rows w, w + 4, ...; for each tile a row's scores are formed with
-// lane = key, its weights with lane = output dim.
+// ------------------------------------------------------ K3: attention ----
+// One workgroup of 4 waves per (unit, group of `hg` kv heads, query chunk,
+// key split).  For each head of the group its rows are the (query position j,
+// q head of the kv group) pairs r = j * group + gh; wave w owns rows w, w + 4,
+// ...  Keys are visited in 64-key tiles that start at multiples of 64 in
+// absolute position, in ascending order, head after head; the tile stream of
+// the whole group runs through one pipeline, so a workgroup fills it once.
+// Each tile goes HBM -> LDS directly (global_load_lds_dwordx4: no VGPR
+// staging, no transposition), each wave issuing a quarter of it; while tile
+// `it` is consumed the next NST-1 tiles are in flight.  Scores are formed with
+// lane = key (K rows read as 16-byte chunks, XOR-swizzled so 16 consecutive
+// rows hit distinct banks), weights with lane = output dim (V kept row-major
+// and read with the gfx950 transposing LDS read, which hands each lane its
+// dim for 4 consecutive keys as two bf16 pairs).
 //
-// APPEND: the call's new frames all belong to this workgroup's query chunk
-// (one chunk per unit), so the workgroup whose key range ends at the newest
-// frame (chunk 0; in split mode the last split) also rotates and writes the
-// new K/V rows of its kv head before it reads the window.  Nothing else reads
-// those rows in this launch, so the launch needs no separate append kernel.
-template <class E, int D, bool MOD, bool SPLIT, bool APPEND>
-__global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, StateTable t) {
-    using L = Lds<E, D>;
-    constexpr int H2 = D / 2, CG = H2 / 4;
-    __shared__ __attribute__((aligned(16))) uint32_t lds[L::TOTAL];
-    uint32_t* Qs = lds + 2 * L::BUF;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t* Pw = Qs + L::QDW + wave * L::PDW;
+// Rows of a tile outside the workgroup's key range are fetched from the
+// nearest in-range row instead: finite values with weight exactly 0, so no
+// zero-fill is needed and uninitialised LDS is never multiplied.
+//
+// APPEND: the new frames of the call all belong to query chunk 0, so the
+// workgroups whose key range ends at the newest frame (chunk 0; in split mode
+// the last split) also rotate and write the new K/V rows of their kv heads
+// before any tile holding them is read.
+template <class E, int D>
+struct Tl {
+    static constexpr int RB = D * E::E;          // bytes per K / V row
+    static constexpr int CPR = RB / 16;          // 16-byte chunks per row
+    static constexpr int TILE = kTile * RB;      // bytes of one K (or V) tile
+    static constexpr int NST = 2;                // LDS stages (tiles)
+    static constexpr int IPW = CPR / 4;          // DMA instructions per wave per K (or V) tile
+    static constexpr int LPW = 2 * IPW;          // DMA instructions per wave per tile
+    static constexpr int PRB = kTile * E::E;     // bytes of one P row
+    static constexpr int QCAP = kQsBytes;        // rotated query rows of the head group
+    static constexpr int BYTES = NST * 2 * TILE + QCAP + 4 * PRB;
+};
+template <int CPR>
+__device__ __forceinline__ int ksw(int r) { return CPR == 8 ? ((r >> 1) & 7) : (r & 15); }
+// V rows: a transposing read covers 4 consecutive rows; XOR the chunk index so
+// those 4 rows fall on distinct banks (128-byte rows pair up as r, r+2; 256-byte
+// rows all start on bank 0).
+template <class E, int CPR>
+__device__ __forceinline__ int vsw(int r) {
+    if constexpr (E::E == 4) return 0;
+    return CPR == 8 ? (((r >> 1) & 1) << 2) : ((r & 3) << 2);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define VRT_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ void dma16(const char* g, char* l) {
+    __builtin_amdgcn_global_load_lds((VRT_GLOBAL void*)(__UINTPTR_TYPE__)g,
+                                     (VRT_LDS void*)(__UINTPTR_TYPE__)l, 16, 0, 0);
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// RPW: rows per wave (1 when a head has at most 4 rows; then the wave's query
+// row of the current head is kept in registers for that head's key loop).
+template <class E, int D, bool MOD, bool SPLIT, bool APPEND, int RPW>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
+    using L = Tl<E, D>;
+    constexpr int H2 = D / 2, CG = H2 / 4, DPL = D / 64;
+    __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+    char* Qs = lds + L::NST * 2 * L::TILE;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+    char* Pw = Qs + L::QCAP + wave * L::PRB;
 
     int b = blockIdx.x;
     const int split = SPLIT ? b % a.n_splits : 0;
     if (SPLIT) b /= a.n_splits;
     const int qc = b % a.n_qchunks;
     b /= a.n_qchunks;
-    const int g = b % a.g.hkv;
-    const int unit = b / a.g.hkv;
+    const int ngb = a.g.hkv / a.hg;
+    const int g0 = (b % ngb) * a.hg;          // first kv head of the group
+    const int unit = b / ngb;
+    const int hg = a.hg;
     const UnitMap& m = a.m;
     const int si = unit / m.nl, li = unit - si * m.nl;
     const long long cu = (long long)t.call_idx[si] * m.nl_call + m.l_off + li;
 
     const int W = a.g.window, group = a.g.group;
-    const long long avail = t.p0[si] - t.n_kv[si];           // abs_base / first position
+    const long long avail = t.p0[si] - t.n_kv[si];             // abs_base / first position
     const long long pq0 = t.p0[si] + (long long)qc * a.qchunk;  // first query of the chunk
     const int nq = min(a.qchunk, m.n - qc * a.qchunk);
-    const int R = nq * group;
+    const int R = nq * group;                                   // rows per head
     long long wlo = max(avail, pq0 - W + 1);
     long long whi = pq0 + nq - 1;
     bool appender = APPEND && qc == 0;
@@ -263,172 +360,163 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, StateTable t) {
     }
 
     char* layer = (char*)t.ring[si] + (long long)(m.layer0 + m.l_off + li) * a.g.layer_bytes;
-    char* Kg = layer + (long long)g * a.g.slice_bytes;
-    char* Vg = Kg + a.g.v_off;
+    const long long tfirst = floor_div(wlo, kTile);
+    const int nt = (int)(floor_div(whi, kTile) - tfirst + 1);   // tiles per head
+    const int ntt = nt * hg;                                    // tiles of the group
 
-    // ---- RoPE angles of the chunk's positions, once, into the second tile
-    // buffer (free until the first tile is committed there)
-    double* cs = (double*)(lds + L::BUF);
-    for (int x = threadIdx.x; x < nq * H2; x += blockDim.x) {
-        const int j = x / H2, i = x - j * H2;
-        rope_angle(pq0 + j, i, D, a.g.theta, &cs[2 * x], &cs[2 * x + 1]);
-    }
-    __syncthreads();
-
-    // ---- new K/V rows of kv head g (fused append)
-    if (APPEND && appender) {
-        constexpr int VCH = D * E::E / 16;
-        const long long row_elems = (long long)a.g.hkv * D;
-        const long long in0 = (cu * m.n_total + m.t0) * row_elems * E::E;
-        const char* kin = (const char*)a.k + in0 + (long long)g * D * E::E;
-        const char* vin = (const char*)a.v + in0 + (long long)g * D * E::E;
-        const int nkv = t.n_kv[si];
-        for (int x = threadIdx.x; x < m.n * CG; x += blockDim.x) {
-            const int c = x % CG, f = x / CG;
-            const long long pos = t.p0[si] + f;
-            const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + f);
-            const char* src = kin + (long long)f * row_elems * E::E;
-            float x0[4], x1[4], y0[4], y1[4];
-            ld4<E>(src + 4 * c * E::E, x0);
-            ld4<E>(src + (H2 + 4 * c) * E::E, x1);
+    // this wave's quarter of the loads of group tile `T` into stage `st`
+    auto issue = [&](int T, int st) {
+        const int hh = T / nt, it = T - hh * nt;
+        const char* Kg = layer + (long long)(g0 + hh) * a.g.slice_bytes;
+        const char* Vg = Kg + a.g.v_off;
+        const long long TB = (tfirst + it) * kTile;
+        const long long sb = MOD ? (TB % a.g.slots) : (TB - avail);
+        const int rlo = (int)max(0LL, wlo - TB), rhi = (int)min(63LL, whi - TB);
+        char* ks = lds + st * 2 * L::TILE;
+        char* vs = ks + L::TILE;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const double* an = cs + 2 * (f * H2 + 4 * c + q);
-                rope_rot(x0[q], x1[q], an[0], an[1], &y0[q], &y1[q]);
-            }
-            char* dst = Kg + slot * (D * E::E);
-            st4<E>(dst + 4 * c * E::E, y0);
-            st4<E>(dst + (H2 + 4 * c) * E::E, y1);
+        for (int i = 0; i < L::IPW; ++i) {
+            const int ins = wave * L::IPW + i;         // instruction index within the tile
+            const int q = ins * 64 + lane;             // 16-byte chunk this lane fills
+            const int r = q / L::CPR, pc = q % L::CPR;
+            const int rr = min(max(r, rlo), rhi);
+            const long long off = (sb + rr) * L::RB;
+            dma16(Kg + off + 16 * (pc ^ ksw<L::CPR>(r)), ks + ins * 1024);
+            dma16(Vg + off + 16 * (pc ^ vsw<E, L::CPR>(r)), vs + ins * 1024);
         }
-        for (int x = threadIdx.x; x < m.n * VCH; x += blockDim.x) {
-            const int c = x % VCH, f = x / VCH;
-            const long long pos = t.p0[si] + f;
-            const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + f);
-            *(uint4*)(Vg + slot * (D * E::E) + 16 * c) =
-                *(const uint4*)(vin + (long long)f * row_elems * E::E + 16 * c);
-        }
+    };
+    // a tile holds new rows iff it reaches the first new frame
+    auto has_new = [&](int T) {
+        const int it = T % nt;
+        return APPEND && appender && (tfirst + it) * kTile + kTile - 1 >= t.p0[si];
+    };
+
+    // tiles without new rows may be fetched before the append
+    bool issued_head = true;
+#pragma unroll
+    for (int st = 0; st < L::NST - 1; ++st) {
+        if (st < ntt && !has_new(st)) issue(st, st);
+        else issued_head = issued_head && st >= ntt;
     }
 
-    // ---- rotated queries -> LDS (dtype E)
+    // ---- rotated queries of every head -> Qs (dtype E); new K/V rows
     {
         const long long qrow = (long long)a.g.hq * D;
+        const long long krow = (long long)a.g.hkv * D;
+        const int nkv = t.n_kv[si];
         for (int x = threadIdx.x; x < R * CG; x += blockDim.x) {
             const int c = x % CG, r = x / CG;
             const int j = r / group, gh = r - j * group;
-            const int hq = g * group + gh;
-            const char* src = (const char*)a.q +
-                              ((cu * m.n_total + m.t0 + (long long)qc * a.qchunk + j) * qrow +
-                               (long long)hq * D) * E::E;
-            float x0[4], x1[4], y0[4], y1[4];
-            ld4<E>(src + 4 * c * E::E, x0);
-            ld4<E>(src + (H2 + 4 * c) * E::E, x1);
+            const long long pos = pq0 + j;
+            const long long frame = m.t0 + (long long)qc * a.qchunk + j;
+            double cs[4], sn[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const double* an = cs + 2 * (j * H2 + 4 * c + q);
-                rope_rot(x0[q], x1[q], an[0], an[1], &y0[q], &y1[q]);
+            for (int q = 0; q < 4; ++q) rope_angle(pos, a.g.omega[4 * c + q], &cs[q], &sn[q]);
+            for (int hh = 0; hh < hg; ++hh) {
+                const int g = g0 + hh;
+                const int hq = g * group + gh;
+                const char* src =
+                    (const char*)a.q + ((cu * m.n_total + frame) * qrow + (long long)hq * D) * E::E;
+                float x0[4], x1[4], y0[4], y1[4];
+                ld4<E>(src + 4 * c * E::E, x0);
+                ld4<E>(src + (H2 + 4 * c) * E::E, x1);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) rope_rot(x0[q], x1[q], cs[q], sn[q], &y0[q], &y1[q]);
+                char* dst = Qs + (hh * R + r) * L::RB;
+                st4<E, false>(dst + 4 * c * E::E, y0);
+                st4<E, false>(dst + (H2 + 4 * c) * E::E, y1);
+                if (APPEND && appender && gh == 0) {
+                    char* Kg = layer + (long long)g * a.g.slice_bytes;
+                    char* Vg = Kg + a.g.v_off;
+                    const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + j);
+                    const char* ksrc =
+                        (const char*)a.k + ((cu * m.n_total + frame) * krow + (long long)g * D) * E::E;
+                    ld4<E>(ksrc + 4 * c * E::E, x0);
+                    ld4<E>(ksrc + (H2 + 4 * c) * E::E, x1);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        rope_rot(x0[q], x1[q], cs[q], sn[q], &y0[q], &y1[q]);
+                    char* kd = Kg + slot * L::RB;
+                    st4<E, true>(kd + 4 * c * E::E, y0);
+                    st4<E, true>(kd + (H2 + 4 * c) * E::E, y1);
+                    const char* vsrc =
+                        (const char*)a.v + ((cu * m.n_total + frame) * krow + (long long)g * D) * E::E;
+#pragma unroll
+                    for (int u = 0; u < L::CPR / CG; ++u) {
+                        const int ch = c + u * CG;
+                        gst<uint4>(Vg + slot * L::RB + 16 * ch, gld<uint4>(vsrc + 16 * ch));
+                    }
+                }
             }
-            char* dst = (char*)(Qs + r * L::ROWDW);
-            st4<E>(dst + 4 * c * E::E, y0);
-            st4<E>(dst + (H2 + 4 * c) * E::E, y1);
         }
     }
-    if (APPEND && appender) __threadfence();   // new rows visible before the window is read
-    __syncthreads();                           // angles consumed; Qs written
+    // appended rows visible to every thread's later loads; Qs written
+    __syncthreads();
+    if (!issued_head) {
+#pragma unroll
+        for (int st = 0; st < L::NST - 1; ++st)
+            if (st < ntt && has_new(st)) issue(st, st);
+    }
 
-    // ---- per-row state (rows w, w+4, w+8, w+12 of this wave)
-    constexpr int RPW = kRows / 4;
-    constexpr int DPL = D / 64;  // output dims per lane
-    float mrow[RPW], lrow[RPW], acc[RPW][DPL];
-    long long rlo[RPW], rhi[RPW];
+    // ---- per-row state.  The softmax denominator is kept per lane (lane =
+    // key position mod 64, rescaled by the row's uniform alpha) and summed
+    // across lanes once, after the head's last tile.
+    float mrow[RPW], lpart[RPW], acc[RPW][DPL];
+    int rlo[RPW], rhi[RPW];                  // row bounds relative to tile 0
+    const long long T0 = tfirst * kTile;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        mrow[i] = kSent;
-        lrow[i] = 0.f;
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) acc[i][k] = 0.f;
-        const int r = wave + 4 * i;
-        const long long pq = pq0 + r / group;
-        rlo[i] = max(wlo, pq - W + 1);
-        rhi[i] = min(whi, pq);
+        const long long pq = pq0 + (wave + 4 * i) / group;
+        rlo[i] = (int)(max(wlo, pq - W + 1) - T0);
+        rhi[i] = (int)(min(whi, pq) - T0);
     }
+    uint4 qreg[RPW == 1 ? L::CPR : 1];
 
-    const long long tfirst = floor_div(wlo, kTile);
-    const int nt = (int)(floor_div(whi, kTile) - tfirst + 1);
-
-    uint4 pk[L::IPT][2], pv[L::IPT][2];
-    auto prefetch = [&](long long tile) {
-        const long long TB = tile * kTile;
-        const long long sb = MOD ? (TB % a.g.slots) : (TB - avail);
+    for (int T = 0; T < ntt; ++T) {
+        const int hh = T / nt, it = T - hh * nt;
+        if (it == 0) {   // head start: reset the rows, load this head's query row
 #pragma unroll
-        for (int it = 0; it < L::IPT; ++it) {
-            const int item = threadIdx.x + it * 256;
-            const int jp = item / L::CPR, c = item - jp * L::CPR;
+            for (int i = 0; i < RPW; ++i) {
+                mrow[i] = kSent;
+                lpart[i] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const long long pos = TB + 2 * jp + r;
-                if (pos >= wlo && pos <= whi) {
-                    const long long off = (sb + 2 * jp + r) * (D * E::E) + 16 * c;
-                    pk[it][r] = *(const uint4*)(Kg + off);
-                    pv[it][r] = *(const uint4*)(Vg + off);
-                } else {
-                    pk[it][r] = make_uint4(0, 0, 0, 0);
-                    pv[it][r] = make_uint4(0, 0, 0, 0);
-                }
+                for (int k = 0; k < DPL; ++k) acc[i][k] = 0.f;
+            }
+            if constexpr (RPW == 1) {
+                const char* qr = Qs + (hh * R + min(wave, R - 1)) * L::RB;
+#pragma unroll
+                for (int c = 0; c < L::CPR; ++c) qreg[c] = *(const uint4*)(qr + 16 * c);
             }
         }
-    };
-    auto commit = [&](int buf) {
-        uint32_t* Kb = lds + buf * L::BUF;
-        uint32_t* Vb = Kb + L::KDW;
-#pragma unroll
-        for (int it = 0; it < L::IPT; ++it) {
-            const int item = threadIdx.x + it * 256;
-            const int jp = item / L::CPR, c = item - jp * L::CPR;
-            *(uint4*)(Kb + (2 * jp) * L::KP + 4 * c) = pk[it][0];
-            *(uint4*)(Kb + (2 * jp + 1) * L::KP + 4 * c) = pk[it][1];
-            const uint32_t w0[4] = {pv[it][0].x, pv[it][0].y, pv[it][0].z, pv[it][0].w};
-            const uint32_t w1[4] = {pv[it][1].x, pv[it][1].y, pv[it][1].z, pv[it][1].w};
-            if constexpr (E::E == 2) {
-                // chunk c holds dims 8c .. 8c+7; V^T word (dim, key pair jp)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
-                    const uint32_t hi = (e & 1) ? (w1[e >> 1] & 0xffff0000u) : (w1[e >> 1] << 16);
-                    Vb[(8 * c + e) * L::VP + jp] = lo | hi;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Vb[(4 * c + e) * L::VP + 2 * jp] = w0[e];
-                    Vb[(4 * c + e) * L::VP + 2 * jp + 1] = w1[e];
-                }
-            }
-        }
-    };
-
-    prefetch(tfirst);
-    commit(0);
-    __syncthreads();
-    for (int it = 0; it < nt; ++it) {
-        if (it + 1 < nt) prefetch(tfirst + it + 1);
-        const uint32_t* Kb = lds + (it & 1) * L::BUF;
-        const uint32_t* Vb = Kb + L::KDW;
-        const long long TB = (tfirst + it) * kTile;
+        // tile T has landed once only the loads issued after it are outstanding
+        if (L::NST > 2 && T + 1 < ntt)
+            wait_vm<(L::NST > 2 ? L::LPW : 0)>();
+        else
+            wait_vm<0>();
+        __syncthreads();   // every wave's share landed; stage of tile T-1 is free
+        if (T + L::NST - 1 < ntt) issue(T + L::NST - 1, (T + L::NST - 1) % L::NST);
+        const char* Ks = lds + (T % L::NST) * 2 * L::TILE;
+        const char* Vs = Ks + L::TILE;
+        const int tb = it * kTile;   // tile start relative to tile 0
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int r = wave + 4 * i;
             if (r >= R) break;
-            const int lo = (int)max(-1LL, min(64LL, rlo[i] - TB));
-            const int hi = (int)max(-1LL, min(64LL, rhi[i] - TB));
+            const int lo = max(-1, min(64, rlo[i] - tb));
+            const int hi = max(-1, min(64, rhi[i] - tb));
             if (hi < 0 || lo > 63 || lo > hi) continue;  // no key of this tile for the row
             // scores: lane = key
             float s = 0.f;
-            const uint32_t* krow = Kb + lane * L::KP;
-            const uint32_t* qrow = Qs + r * L::ROWDW;
+            const char* krow_l = Ks + lane * L::RB;
+            const char* qr = Qs + (hh * R + r) * L::RB;
 #pragma unroll
-            for (int c4 = 0; c4 < L::ROWDW / 4; ++c4) {
-                const uint4 kv = *(const uint4*)(krow + 4 * c4);
-                const uint4 qv = *(const uint4*)(qrow + 4 * c4);
+            for (int c = 0; c < L::CPR; ++c) {
+                const uint4 kv = *(const uint4*)(krow_l + 16 * (c ^ ksw<L::CPR>(lane)));
+                uint4 qv;
+                if constexpr (RPW == 1)
+                    qv = qreg[c];
+                else
+                    qv = *(const uint4*)(qr + 16 * c);
                 if constexpr (E::E == 2) {
                     s = dot2bf(kv.x, qv.x, s);
                     s = dot2bf(kv.y, qv.y, s);
@@ -447,75 +535,83 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, StateTable t) {
             const float mn = fmaxf(mrow[i], mt);
             const float alpha = fast_exp2(mrow[i] - mn);
             const float p = valid ? fast_exp2(sv - mn) : 0.f;
-            lrow[i] = __fmaf_rn(lrow[i], alpha, wave_sum(p));
+            lpart[i] = __fmaf_rn(lpart[i], alpha, p);
             mrow[i] = mn;
-            if constexpr (E::E == 2) {
-                ((uint16_t*)Pw)[lane] = (uint16_t)to_bf16(p);
-            } else {
-                ((float*)Pw)[lane] = p;
-            }
+            if constexpr (E::E == 2)
+                *(uint16_t*)(Pw + 2 * lane) = (uint16_t)to_bf16(p);
+            else
+                *(float*)(Pw + 4 * lane) = p;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // weights: lane = output dim
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) {
-                const uint32_t* vrow = Vb + (lane + 64 * k) * L::VP;
-                float o = acc[i][k] * alpha;
+            for (int h = 0; h < DPL; ++h) {
+                float o = acc[i][h] * alpha;
+                if constexpr (E::E == 2) {
 #pragma unroll
-                for (int c4 = 0; c4 < kTile * E::E / 16; ++c4) {
-                    const uint4 vv = *(const uint4*)(vrow + 4 * c4);
-                    const uint4 pp = *(const uint4*)(Pw + 4 * c4);
-                    if constexpr (E::E == 2) {
+                    for (int kb = 0; kb < 16; ++kb) {
+                        // keys 4kb .. 4kb+3 of dim 64h + lane, as two bf16 pairs
+                        const int row = 4 * kb + ((lane & 15) >> 2);
+                        const int byte = 2 * (64 * h + 16 * (lane >> 4) + 4 * (lane & 3));
+                        const int ch = (byte >> 4) ^ vsw<E, L::CPR>(row);
+                        const v4i16 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (VRT_LDS v4i16*)(__UINTPTR_TYPE__)(Vs + row * L::RB + 16 * ch + (byte & 15)));
+                        const uint2 vv = __builtin_bit_cast(uint2, r4);
+                        const uint2 pp = *(const uint2*)(Pw + 8 * kb);
                         o = dot2bf(pp.x, vv.x, o);
                         o = dot2bf(pp.y, vv.y, o);
-                        o = dot2bf(pp.z, vv.z, o);
-                        o = dot2bf(pp.w, vv.w, o);
-                    } else {
-                        o = __fmaf_rn(__uint_as_float(pp.x), __uint_as_float(vv.x), o);
-                        o = __fmaf_rn(__uint_as_float(pp.y), __uint_as_float(vv.y), o);
-                        o = __fmaf_rn(__uint_as_float(pp.z), __uint_as_float(vv.z), o);
-                        o = __fmaf_rn(__uint_as_float(pp.w), __uint_as_float(vv.w), o);
+                    }
+                } else {
+#pragma unroll 4
+                    for (int j = 0; j < kTile; j += 4) {
+                        const float4 pp = *(const float4*)(Pw + 4 * j);
+                        const float* vc = (const float*)(Vs + 4 * (64 * h + lane));
+                        o = __fmaf_rn(pp.x, vc[(j + 0) * D], o);
+                        o = __fmaf_rn(pp.y, vc[(j + 1) * D], o);
+                        o = __fmaf_rn(pp.z, vc[(j + 2) * D], o);
+                        o = __fmaf_rn(pp.w, vc[(j + 3) * D], o);
                     }
                 }
-                acc[i][k] = o;
+                acc[i][h] = o;
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        if (it + 1 < nt) commit((it + 1) & 1);
-        __syncthreads();
-    }
 
-    // ---- epilogue
+        if (it == nt - 1) {   // ---- head epilogue
+            const int g = g0 + hh;
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int r = wave + 4 * i;
-        if (r >= R) break;
-        const int j = r / group, gh = r - j * group;
-        if (SPLIT) {
-            float* pr = a.partials +
-                        (((cu * a.g.hkv + g) * a.n_splits + split) * group + r) * (long long)(2 + D);
-            if (lane == 0) {
-                pr[0] = mrow[i];
-                pr[1] = lrow[i];
-            }
+            for (int i = 0; i < RPW; ++i) {
+                const int r = wave + 4 * i;
+                if (r >= R) break;
+                const float lrow = wave_sum(lpart[i]);
+                const int j = r / group, gh = r - j * group;
+                if (SPLIT) {
+                    float* pr = a.partials +
+                                (((cu * a.g.hkv + g) * a.n_splits + split) * group + r) * (long long)(2 + D);
+                    if (lane == 0) {
+                        gst<float>(pr, mrow[i]);
+                        gst<float>(pr + 1, lrow);
+                    }
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) pr[2 + lane + 64 * k] = acc[i][k];
-        } else {
-            const int hq = g * group + gh;
-            char* dst = (char*)a.out +
-                        ((cu * m.n_total + m.t0 + (long long)qc * a.qchunk + j) * a.g.hq + hq) *
-                            (long long)D * E::E;
+                    for (int k = 0; k < DPL; ++k) gst<float>(pr + 2 + lane + 64 * k, acc[i][k]);
+                } else {
+                    const int hq = g * group + gh;
+                    char* dst = (char*)a.out +
+                                ((cu * m.n_total + m.t0 + (long long)qc * a.qchunk + j) * a.g.hq + hq) *
+                                    (long long)D * E::E;
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) {
-                const float o = acc[i][k] / lrow[i];
-                const int d = lane + 64 * k;
-                if constexpr (E::E == 2)
-                    ((uint16_t*)dst)[d] = (uint16_t)to_bf16(o);
-                else
-                    ((float*)dst)[d] = o;
+                    for (int k = 0; k < DPL; ++k) {
+                        const float o = acc[i][k] / lrow;
+                        const int d = lane + 64 * k;
+                        if constexpr (E::E == 2)
+                            gst<uint16_t>(dst + 2 * d, (uint16_t)to_bf16(o));
+                        else
+                            gst<float>(dst + 4 * d, o);
+                    }
+                }
             }
         }
     }
@@ -541,16 +637,16 @@ __global__ __launch_bounds__(64) void k_dec_combine(AttnArgs a, StateTable t) {
     const int group = a.g.group;
     const float* base = a.partials + ((cu * a.g.hkv + g) * a.n_splits) * group * (long long)(2 + D);
     float M = kSent;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[((long long)s * group + r) * (2 + D)]);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, gld<float>(base + ((long long)s * group + r) * (2 + D)));
     float Lsum = 0.f, o[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) o[k] = 0.f;
     for (int s = 0; s < ns; ++s) {
         const float* pr = base + ((long long)s * group + r) * (2 + D);
-        const float w = fast_exp2(pr[0] - M);
-        Lsum = __fmaf_rn(pr[1], w, Lsum);
+        const float w = fast_exp2(gld<float>(pr) - M);
+        Lsum = __fmaf_rn(gld<float>(pr + 1), w, Lsum);
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) o[k] = __fmaf_rn(pr[2 + lane + 64 * k], w, o[k]);
+        for (int k = 0; k < DPL; ++k) o[k] = __fmaf_rn(gld<float>(pr + 2 + lane + 64 * k), w, o[k]);
     }
     char* dst = (char*)a.out + ((cu * m.n_total + m.t0) * a.g.hq + hq) * (long long)D * E::E;
 #pragma unroll
@@ -558,9 +654,9 @@ __global__ __launch_bounds__(64) void k_dec_combine(AttnArgs a, StateTable t) {
         const float v = o[k] / Lsum;
         const int d = lane + 64 * k;
         if constexpr (E::E == 2)
-            ((uint16_t*)dst)[d] = (uint16_t)to_bf16(v);
+            gst<uint16_t>(dst + 2 * d, (uint16_t)to_bf16(v));
         else
-            ((float*)dst)[d] = v;
+            gst<float>(dst + 4 * d, v);
     }
 }
 
@@ -590,24 +686,27 @@ hipError_t launch_rope_append(const AppendArgs& a, const StateTable& t, hipStrea
 
 hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t s) {
     const long long blocks =
-        (long long)a.m.n_states * a.m.nl * a.g.hkv * a.n_qchunks * a.n_splits;
-    const dim3 grid((unsigned)blocks);
+        (long long)a.m.n_states * a.m.nl * (a.g.hkv / a.hg) * a.n_qchunks * a.n_splits;
+    const dim3 grid((unsigned)blocks), block(256);
     const bool split = a.n_splits > 1 || a.partials != nullptr;
     const bool app = a.append != 0;
+    const bool one = (long long)std::min(a.qchunk, a.m.n) * a.g.group <= 4;  // <= 1 row per wave
+#define VRT_ATTN(MOD, SPLIT, APP)                                                                   \
+    do {                                                                                            \
+        if (one)                                                                                    \
+            hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, 1>), grid, block, 0, s, a, t);      \
+        else                                                                                        \
+            hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, kRows / 4>), grid, block, 0, s, a, t); \
+    } while (0)
     VRT_DISPATCH_ED(a.g.dtype, a.g.D, {
-        if (a.g.mod && split && app)
-            hipLaunchKernelGGL((k_attn_valu<E_, D_, true, true, true>), grid, dim3(256), 0, s, a, t);
-        else if (a.g.mod && split)
-            hipLaunchKernelGGL((k_attn_valu<E_, D_, true, true, false>), grid, dim3(256), 0, s, a, t);
-        else if (a.g.mod && app)
-            hipLaunchKernelGGL((k_attn_valu<E_, D_, true, false, true>), grid, dim3(256), 0, s, a, t);
-        else if (a.g.mod)
-            hipLaunchKernelGGL((k_attn_valu<E_, D_, true, false, false>), grid, dim3(256), 0, s, a, t);
-        else if (app)
-            hipLaunchKernelGGL((k_attn_valu<E_, D_, false, false, true>), grid, dim3(256), 0, s, a, t);
-        else
-            hipLaunchKernelGGL((k_attn_valu<E_, D_, false, false, false>), grid, dim3(256), 0, s, a, t);
+        if (a.g.mod && split && app) VRT_ATTN(true, true, true);
+        else if (a.g.mod && split) VRT_ATTN(true, true, false);
+        else if (a.g.mod && app) VRT_ATTN(true, false, true);
+        else if (a.g.mod) VRT_ATTN(true, false, false);
+        else if (app) VRT_ATTN(false, false, true);
+        else VRT_ATTN(false, false, false);
     });
+#undef VRT_ATTN
     return hipGetLastError();
 }
 
