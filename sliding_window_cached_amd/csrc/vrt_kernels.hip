@@ -89,8 +89,20 @@ __device__ __forceinline__ long long floor_div(long long a, long long b) {
 // ---------------------------------------------------------------- RoPE ----
 // angle = pos * omega_i in fp64 (a float32 angle is off by up to ~0.03 rad at
 // positions near 1e6); omega_i = theta^(-2i/D) comes from the host in fp64.
+// The angle is first reduced by multiples of 2*pi with the additive method of
+// Cody and Waite (1980): 2*pi is split into three doubles, the first two with
+// 30 significant bits, so k*c1 and k*c2 are exact for |k| < 2^23 and the three
+// fused steps leave the reduced angle accurate to about one ulp.  sincos then
+// runs on an argument in [-pi, pi]; beyond |x| = 2.6e7 the library reduces it.
 __device__ __forceinline__ void rope_angle(long long pos, double omega, double* c, double* s) {
-    sincos((double)pos * omega, s, c);
+    double x = (double)pos * omega;
+    if (fabs(x) < 2.6e7) {
+        const double k = rint(x * 0.15915494309189535);  // x / (2 pi), nearest integer
+        x = fma(-k, 6.283185303211212, x);
+        x = fma(-k, 3.9683743166540886e-09, x);
+        x = fma(-k, 2.068073192717642e-18, x);
+    }
+    sincos(x, s, c);
 }
 
 // NEOX pair (i, i + D/2): y0 = x0 cos - x1 sin, y1 = x1 cos + x0 sin, in fp64,
@@ -286,7 +298,7 @@ struct Tl {
     static constexpr int RB = D * E::E;          // bytes per K / V row
     static constexpr int CPR = RB / 16;          // 16-byte chunks per row
     static constexpr int TILE = kTile * RB;      // bytes of one K (or V) tile
-    static constexpr int NST = 2;                // LDS stages (tiles)
+    static constexpr int NST = 2;                // LDS stages (tiles); T+1 streams while T is read
     static constexpr int IPW = CPR / 4;          // DMA instructions per wave per K (or V) tile
     static constexpr int LPW = 2 * IPW;          // DMA instructions per wave per tile
     static constexpr int PRB = kTile * E::E;     // bytes of one P row
@@ -391,72 +403,89 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         return APPEND && appender && (tfirst + it) * kTile + kTile - 1 >= t.p0[si];
     };
 
-    // tiles without new rows may be fetched before the append
-    bool issued_head = true;
+    // ---- prologue: rotated queries of every head -> Qs (dtype E) and the new
+    // K/V rows.  One (head, row, 4-pair group) item per thread, so every input
+    // load is independent; each thread's first item is loaded before the tile
+    // DMAs go out, so those loads do not queue behind the tiles.
+    const long long qrow = (long long)a.g.hq * D;
+    const long long krow = (long long)a.g.hkv * D;
+    const int nkv = t.n_kv[si];
+    const int items = hg * R * CG;
+    struct Item {
+        float x0[4], x1[4], k0[4], k1[4];
+        uint4 vch[L::CPR / CG];
+    };
+    auto load_item = [&](int x, Item& it) {
+        const int c = x % CG, r = (x / CG) % R, hh = x / (CG * R);
+        const int j = r / group, gh = r - j * group;
+        const int g = g0 + hh;
+        const long long frame = m.t0 + (long long)qc * a.qchunk + j;
+        const char* src = (const char*)a.q +
+                          ((cu * m.n_total + frame) * qrow + (long long)(g * group + gh) * D) * E::E;
+        ld4<E>(src + 4 * c * E::E, it.x0);
+        ld4<E>(src + (H2 + 4 * c) * E::E, it.x1);
+        if (APPEND && appender && gh == 0) {
+            const long long kv0 = ((cu * m.n_total + frame) * krow + (long long)g * D) * E::E;
+            ld4<E>((const char*)a.k + kv0 + 4 * c * E::E, it.k0);
+            ld4<E>((const char*)a.k + kv0 + (H2 + 4 * c) * E::E, it.k1);
 #pragma unroll
-    for (int st = 0; st < L::NST - 1; ++st) {
-        if (st < ntt && !has_new(st)) issue(st, st);
-        else issued_head = issued_head && st >= ntt;
+            for (int u = 0; u < L::CPR / CG; ++u)
+                it.vch[u] = gld<uint4>((const char*)a.v + kv0 + 16 * (c + u * CG));
+        }
+    };
+    auto finish_item = [&](int x, const Item& it) {
+        const int c = x % CG, r = (x / CG) % R, hh = x / (CG * R);
+        const int j = r / group, gh = r - j * group;
+        const int g = g0 + hh;
+        const long long pos = pq0 + j;
+        double cs[4], sn[4];
+        float y0[4], y1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rope_angle(pos, a.g.omega[4 * c + q], &cs[q], &sn[q]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rope_rot(it.x0[q], it.x1[q], cs[q], sn[q], &y0[q], &y1[q]);
+        char* dst = Qs + (hh * R + r) * L::RB;
+        st4<E, false>(dst + 4 * c * E::E, y0);
+        st4<E, false>(dst + (H2 + 4 * c) * E::E, y1);
+        if (APPEND && appender && gh == 0) {
+            char* Kg = layer + (long long)g * a.g.slice_bytes;
+            char* Vg = Kg + a.g.v_off;
+            const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + j);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rope_rot(it.k0[q], it.k1[q], cs[q], sn[q], &y0[q], &y1[q]);
+            char* kd = Kg + slot * L::RB;
+            st4<E, true>(kd + 4 * c * E::E, y0);
+            st4<E, true>(kd + (H2 + 4 * c) * E::E, y1);
+#pragma unroll
+            for (int u = 0; u < L::CPR / CG; ++u)
+                gst<uint4>(Vg + slot * L::RB + 16 * (c + u * CG), it.vch[u]);
+        }
+    };
+    Item first;
+    const int x0i = threadIdx.x;
+    if (x0i < items) load_item(x0i, first);
+
+    // Tiles without new rows may be fetched before the append: both stages are
+    // free at the start, so up to two tiles go out ahead of the prologue.
+    constexpr int PRE = L::NST;
+    bool pre_done[PRE];
+#pragma unroll
+    for (int st = 0; st < PRE; ++st) {
+        pre_done[st] = st < ntt && !has_new(st);
+        if (pre_done[st]) issue(st, st);
     }
 
-    // ---- rotated queries of every head -> Qs (dtype E); new K/V rows
-    {
-        const long long qrow = (long long)a.g.hq * D;
-        const long long krow = (long long)a.g.hkv * D;
-        const int nkv = t.n_kv[si];
-        for (int x = threadIdx.x; x < R * CG; x += blockDim.x) {
-            const int c = x % CG, r = x / CG;
-            const int j = r / group, gh = r - j * group;
-            const long long pos = pq0 + j;
-            const long long frame = m.t0 + (long long)qc * a.qchunk + j;
-            double cs[4], sn[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) rope_angle(pos, a.g.omega[4 * c + q], &cs[q], &sn[q]);
-            for (int hh = 0; hh < hg; ++hh) {
-                const int g = g0 + hh;
-                const int hq = g * group + gh;
-                const char* src =
-                    (const char*)a.q + ((cu * m.n_total + frame) * qrow + (long long)hq * D) * E::E;
-                float x0[4], x1[4], y0[4], y1[4];
-                ld4<E>(src + 4 * c * E::E, x0);
-                ld4<E>(src + (H2 + 4 * c) * E::E, x1);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) rope_rot(x0[q], x1[q], cs[q], sn[q], &y0[q], &y1[q]);
-                char* dst = Qs + (hh * R + r) * L::RB;
-                st4<E, false>(dst + 4 * c * E::E, y0);
-                st4<E, false>(dst + (H2 + 4 * c) * E::E, y1);
-                if (APPEND && appender && gh == 0) {
-                    char* Kg = layer + (long long)g * a.g.slice_bytes;
-                    char* Vg = Kg + a.g.v_off;
-                    const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + j);
-                    const char* ksrc =
-                        (const char*)a.k + ((cu * m.n_total + frame) * krow + (long long)g * D) * E::E;
-                    ld4<E>(ksrc + 4 * c * E::E, x0);
-                    ld4<E>(ksrc + (H2 + 4 * c) * E::E, x1);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        rope_rot(x0[q], x1[q], cs[q], sn[q], &y0[q], &y1[q]);
-                    char* kd = Kg + slot * L::RB;
-                    st4<E, true>(kd + 4 * c * E::E, y0);
-                    st4<E, true>(kd + (H2 + 4 * c) * E::E, y1);
-                    const char* vsrc =
-                        (const char*)a.v + ((cu * m.n_total + frame) * krow + (long long)g * D) * E::E;
-#pragma unroll
-                    for (int u = 0; u < L::CPR / CG; ++u) {
-                        const int ch = c + u * CG;
-                        gst<uint4>(Vg + slot * L::RB + 16 * ch, gld<uint4>(vsrc + 16 * ch));
-                    }
-                }
-            }
-        }
+    if (x0i < items) finish_item(x0i, first);
+    for (int x = x0i + blockDim.x; x < items; x += blockDim.x) {
+        Item more;
+        load_item(x, more);
+        finish_item(x, more);
     }
     // appended rows visible to every thread's later loads; Qs written
     __syncthreads();
-    if (!issued_head) {
 #pragma unroll
-        for (int st = 0; st < L::NST - 1; ++st)
-            if (st < ntt && has_new(st)) issue(st, st);
-    }
+    for (int st = 0; st < PRE; ++st)
+        if (st < ntt && !pre_done[st]) issue(st, st);
 
     // ---- per-row state.  The softmax denominator is kept per lane (lane =
     // key position mod 64, rescaled by the row's uniform alpha) and summed
@@ -488,13 +517,15 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
                 for (int c = 0; c < L::CPR; ++c) qreg[c] = *(const uint4*)(qr + 16 * c);
             }
         }
-        // tile T has landed once only the loads issued after it are outstanding
-        if (L::NST > 2 && T + 1 < ntt)
-            wait_vm<(L::NST > 2 ? L::LPW : 0)>();
+        // Outstanding here: tile T, plus tile 1 when T = 0 (tiles 0 and 1 were
+        // both issued, in that order, before the loop).  Tile T+1 (T >= 1) goes
+        // out only after the barrier frees its stage.
+        if (T == 0 && ntt > 1)
+            wait_vm<L::LPW>();
         else
             wait_vm<0>();
-        __syncthreads();   // every wave's share landed; stage of tile T-1 is free
-        if (T + L::NST - 1 < ntt) issue(T + L::NST - 1, (T + L::NST - 1) % L::NST);
+        __syncthreads();   // every wave's share of T landed; T-1's stage is free
+        if (T >= 1 && T + 1 < ntt) issue(T + 1, (T + 1) % L::NST);
         const char* Ks = lds + (T % L::NST) * 2 * L::TILE;
         const char* Vs = Ks + L::TILE;
         const int tb = it * kTile;   // tile start relative to tile 0
