@@ -150,10 +150,15 @@ vrt_status vrt_stream_state_query(const vrt_stream_state* st, int layer, int64_t
 vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32_t* n_kv,
                             int n_new, int32_t* n_compactions);
 
-/* Which attention path a sub-batch of n queries takes: 0 = VALU kernel,
- * 1 = MFMA kernel.  A pure function of (dtype, n): fp32 always 0; bf16 takes
- * 1 when n >= 32.  Results are bit-identical under any chunking that keeps
- * every sub-batch on the same path. */
+/* Which attention path a sub-batch of n frames takes: 0 = vector-ALU kernel
+ * (fp32 dot products), 1 = matrix-core kernel (bf16 MFMA products, fp32
+ * accumulation).  A pure function of the desc and n: 1 exactly for encoder
+ * descs with bf16 storage, head_dim 64, n_heads_q == n_heads_kv and n >= 32;
+ * 0 otherwise; -1 for an invalid desc or n < 1.  A feed is split into
+ * sub-batches of at most max_batch frames and each takes its own path; the
+ * offline call is one sub-batch of T frames.  Outputs are bit-identical
+ * under any chunking whose sub-batches all take the same path; the two paths
+ * agree within bf16 rounding. */
 int vrt_attn_path(const vrt_cache_desc* desc, int n);
 
 /* Offline windowed attention over one whole sequence (streaming-plan page,

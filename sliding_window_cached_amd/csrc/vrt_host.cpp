@@ -101,6 +101,7 @@ Geom make_geom(const vrt_cache_desc& d) {
 
 float scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
 
+
 // kv heads per attention workgroup: the largest divisor of hkv whose rotated
 // query rows fit the workgroup's LDS budget and that still leaves about four
 // workgroups per compute unit, so each workgroup streams a long run of tiles
@@ -121,6 +122,39 @@ int pick_hg(const Geom& g, long long units, int rows_per_head, long long qchunks
         best = h;
     }
     return best;
+}
+
+// Arithmetic path of one sub-batch of n frames: a pure function of the cache
+// description and n, so two feeds that split a sequence differently but take
+// the same path produce bit-identical outputs.
+bool use_mfma(const vrt_cache_desc& d, int n) {
+    return d.kind == VRT_ENC_RING && d.dtype == VRT_BF16 && d.head_dim == 64 &&
+           d.n_heads_q == d.n_heads_kv && n >= kMfmaMinFrames;
+}
+
+// Attention launch parameters of a sub-batch of n frames over `units` units.
+void attn_shape(const Geom& g, bool mfma, long long units, int n, AttnArgs* at) {
+    at->partials = nullptr;
+    at->n_splits = 1;
+    at->split_len = kSplitLen;
+    at->scale_log2 = scale_log2(g.D);
+    if (mfma) {
+        at->qchunk = kQTileMfma;
+        at->n_qchunks = (n + kQTileMfma - 1) / kQTileMfma;
+        at->append = 0;
+        at->hg = 1;
+        return;
+    }
+    at->qchunk = kRows / g.group;
+    at->n_qchunks = (n + at->qchunk - 1) / at->qchunk;
+    // one query chunk per unit: the attention launch appends the new rows
+    // itself; otherwise a separate append launch runs first
+    at->append = at->n_qchunks == 1 ? 1 : 0;
+    at->hg = pick_hg(g, units, std::min(at->qchunk, n) * g.group, at->n_qchunks, 1);
+}
+
+hipError_t launch_attn(const AttnArgs& at, bool mfma, const StateTable& t, hipStream_t s) {
+    return mfma ? launch_attn_mfma(at, t, s) : launch_attn_valu(at, t, s);
 }
 
 // Common checks for the batched calls.  Pure: touches nothing.
@@ -346,9 +380,8 @@ vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32
 }
 
 int vrt_attn_path(const vrt_cache_desc* desc, int n) {
-    (void)desc;
-    (void)n;
-    return 0;
+    if (check_desc(desc) != VRT_OK || n < 1) return -1;
+    return use_mfma(*desc, n) ? 1 : 0;
 }
 
 size_t vrt_offline_scratch_bytes(const vrt_cache_desc* desc, int T) {
@@ -399,15 +432,10 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
     at.k = k;
     at.v = v;
     at.out = out;
-    at.partials = nullptr;
-    at.qchunk = kRows / g.group;
-    at.n_qchunks = (T + at.qchunk - 1) / at.qchunk;
-    at.n_splits = 1;
-    at.split_len = kSplitLen;
-    at.scale_log2 = scale_log2(desc->head_dim);
-    at.append = 0;
-    at.hg = pick_hg(g, 1, std::min(at.qchunk, T) * g.group, at.n_qchunks, 1);
-    if (note(launch_attn_valu(at, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    const bool mfma = use_mfma(*desc, T);
+    attn_shape(g, mfma, 1, T, &at);
+    at.append = 0;   // the append above already wrote every row
+    if (note(launch_attn(at, mfma, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
     return VRT_OK;
 }
 
@@ -450,19 +478,10 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
             at.k = k;
             at.v = v;
             at.out = out;
-            at.partials = nullptr;
-            at.qchunk = kRows / g.group;
-            at.n_qchunks = (m + at.qchunk - 1) / at.qchunk;
-            at.n_splits = 1;
-            at.split_len = kSplitLen;
-            at.scale_log2 = scale_log2(d.head_dim);
-            // one query chunk per unit: the attention launch appends the
-            // new rows itself; otherwise a separate append launch runs first
-            at.append = at.n_qchunks == 1 ? 1 : 0;
-            at.hg = pick_hg(g, (long long)um.n_states * um.nl, std::min(at.qchunk, m) * g.group,
-                            at.n_qchunks, 1);
+            const bool mfma = use_mfma(d, m);
+            attn_shape(g, mfma, (long long)um.n_states * um.nl, m, &at);
             if ((!at.append && note(launch_rope_append(aa, t, stream)) != hipSuccess) ||
-                note(launch_attn_valu(at, t, stream)) != hipSuccess) {
+                note(launch_attn(at, mfma, t, stream)) != hipSuccess) {
                 poison(st, n_states);
                 return VRT_ERR_DEVICE;
             }

@@ -20,6 +20,11 @@ constexpr int kTile = 64;
 constexpr int kRows = 16;
 // LDS bytes for the rotated query rows of a workgroup's kv-head group.
 constexpr int kQsBytes = 6144;
+// Sub-batches of at least this many frames take the matrix-core path (bf16,
+// head_dim 64, one query head per kv head); smaller ones the VALU path.
+constexpr int kMfmaMinFrames = 32;
+// Queries per workgroup of the matrix-core path.
+constexpr int kQTileMfma = 128;
 // Keys per split of the decode step; splits start at multiples of this in
 // absolute position and are merged in ascending order.
 constexpr int kSplitLen = 1024;
@@ -103,6 +108,7 @@ struct CompactArgs {
 
 hipError_t launch_rope_append(const AppendArgs& a, const StateTable& t, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t s);
 hipError_t launch_dec_combine(const AttnArgs& a, const StateTable& t, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, const CompactTable& t, hipStream_t s);
 

@@ -10,7 +10,7 @@
 //                  (streaming-plan page, "Unbounded length": compact_enc_ring).
 //                  Source and destination may overlap; every chunk is staged
 //                  through LDS before any of it is written back.
-//   k_attn_valu    windowed-causal attention, fp32 accumulation: a query at
+//   k_attn         windowed-causal attention, fp32 accumulation: a query at
 //                  absolute position p sees keys in (p - W, p].  Keys are
 //                  visited in 64-key tiles that start at multiples of 64 in
 //                  absolute position, in ascending order; keys outside a
@@ -19,6 +19,9 @@
 //                  result does not depend on which other queries share its
 //                  workgroup, on ring slots or on compaction: chunked feeding
 //                  reproduces the offline pass bit for bit.
+//   k_attn_mfma    the same attention for sub-batches of 32 or more bf16
+//                  frames (the catch-up path), with both products on the
+//                  matrix cores and the same absolute tile grid.
 //   k_dec_combine  log-sum-exp merge of split-K partials in ascending split
 //                  order (decode step).
 //
@@ -648,6 +651,323 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     }
 }
 
+// ------------------------------------------------ K4: attention, MFMA ----
+// The same windowed-causal attention for large sub-batches (the catch-up
+// path): bf16 storage, head_dim 64, one query head per kv head.  One
+// workgroup of 4 waves per (unit, head, tile of 128 queries); wave w owns
+// queries 32w .. 32w+31 of the tile.  Both products run on the bf16 matrix
+// cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation) in transposed form:
+//   S^T = K Q^T      (32 keys x 32 queries per block; lane = query, so the
+//                    softmax of a query is local to the lane and its partner
+//                    lane in the other half of the wave)
+//   O^T += V^T P^T   (32 dims x 32 queries; V^T is read from LDS with the
+//                    transposing read, P^T is S^T's registers, packed)
+// With the MFMA result layout (lane l, register r: key 8(r/4) + 4(l/32) +
+// r%4 of the block, query l%32), registers 8c .. 8c+7 of a lane hold the
+// eight keys that lane contributes to the k = 16 product of key group c; the
+// V^T operand is read with the same key order.
+//
+// Keys stream through LDS in 64-key tiles aligned to absolute position (the
+// same tiles and clamped-row fetch as the VALU kernel); a 32-key half-tile
+// outside the band of all 32 queries of a wave is skipped, which is exact:
+// such a half-tile would only add zero weights.  Every per-query step (the
+// two MFMA chains, the running max, the per-lane partial sums, the rescale)
+// depends only on that query's own window and the absolute tile grid, so the
+// result does not depend on how frames were batched.
+//
+// Queries are rotated in the prologue: the angle p * omega_i is formed and
+// reduced by 2 pi in fp64 as for the keys, then sin and cos are taken in fp32
+// on the reduced angle (error ~3e-7 rad, far below the bf16 rounding of the
+// rotated query that follows).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct M4 {
+    static constexpr int D = 64;
+    static constexpr int RB = 128;                // bytes per K / V row
+    static constexpr int CPR = 8;                 // 16-byte chunks per row
+    static constexpr int QW = 32;                 // queries per wave
+    static constexpr int QT = 4 * QW;             // queries per workgroup
+    static constexpr int TILE = kTile * RB;       // 8 KB
+    static constexpr int NST = 3;                 // LDS stages
+    static constexpr int IPW = TILE / (4 * 1024); // DMA instructions per wave per K (or V) tile
+    static constexpr int LPW = 2 * IPW;
+    static constexpr int BYTES = NST * 2 * TILE;
+};
+static_assert(M4::QT == kQTileMfma, "query tile of the MFMA path");
+
+__device__ __forceinline__ void rope_angle_q(double pos, double omega, float* c, float* s) {
+    double x = pos * omega;
+    if (fabs(x) < 2.6e7) {
+        const double k = rint(x * 0.15915494309189535);
+        x = fma(-k, 6.283185303211212, x);
+        x = fma(-k, 3.9683743166540886e-09, x);
+        x = fma(-k, 2.068073192717642e-18, x);
+        sincosf((float)x, s, c);
+    } else {
+        double sd, cd;
+        sincos(x, &sd, &cd);
+        *s = (float)sd;
+        *c = (float)cd;
+    }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
+    using L = M4;
+    __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int jq = lane & 31;        // query of the lane within the wave
+    const int hf = lane >> 5;        // half of the wave
+
+    // Workgroup -> (unit, head, query tile).  Workgroups are dispatched to the
+    // 8 XCDs round robin; consecutive logical ids (the query tiles of one
+    // (unit, head), which read overlapping key windows) are placed on the same
+    // XCD so its L2 serves the overlap.
+    int b;
+    {
+        const int nb = gridDim.x, x = blockIdx.x & 7, s = blockIdx.x >> 3;
+        const int base = nb >> 3, rem = nb & 7;
+        b = x < rem ? x * (base + 1) + s : rem * (base + 1) + (x - rem) * base + s;
+    }
+    const int qc = b % a.n_qchunks;
+    b /= a.n_qchunks;
+    const int g = b % a.g.hkv;
+    const int unit = b / a.g.hkv;
+    const UnitMap& m = a.m;
+    const int si = unit / m.nl, li = unit - si * m.nl;
+    const long long cu = (long long)t.call_idx[si] * m.nl_call + m.l_off + li;
+
+    const int W = a.g.window;
+    const long long avail = t.p0[si] - t.n_kv[si];
+    const long long pq0 = t.p0[si] + (long long)qc * L::QT;
+    const int nq = min(L::QT, m.n - qc * L::QT);
+    const long long wlo = max(avail, pq0 - W + 1);
+    const long long whi = pq0 + nq - 1;
+    const long long tfirst = floor_div(wlo, kTile);
+    const int ntt = (int)(floor_div(whi, kTile) - tfirst + 1);
+    const long long T0 = tfirst * kTile;
+
+    char* layer = (char*)t.ring[si] + (long long)(m.layer0 + m.l_off + li) * a.g.layer_bytes;
+    const char* Kg = layer + (long long)g * a.g.slice_bytes;
+    const char* Vg = Kg + a.g.v_off;
+
+    auto issue = [&](int T, int st) {
+        const long long TB = T0 + (long long)T * kTile;
+        const long long sb = TB - avail;
+        const int rlo = (int)max(0LL, wlo - TB), rhi = (int)min(63LL, whi - TB);
+        char* ks = lds + st * 2 * L::TILE;
+        char* vs = ks + L::TILE;
+#pragma unroll
+        for (int i = 0; i < L::IPW; ++i) {
+            const int ins = wave * L::IPW + i;
+            const int q = ins * 64 + lane;
+            const int r = q / L::CPR, pc = q % L::CPR;
+            const int rr = min(max(r, rlo), rhi);
+            const long long off = (sb + rr) * L::RB;
+            dma16(Kg + off + 16 * (pc ^ ksw<L::CPR>(r)), ks + ins * 1024);
+            dma16(Vg + off + 16 * (pc ^ vsw<BF16T, L::CPR>(r)), vs + ins * 1024);
+        }
+    };
+
+    // ---- this wave's queries; lanes past the last query repeat it
+    const int qw0 = wave * L::QW;
+    const int nqw = min(L::QW, nq - qw0);   // may be <= 0 for the last tile
+    const int jj = max(0, min(jq, nqw - 1));
+    const long long pq = pq0 + qw0 + jj;
+    const long long frame = m.t0 + (long long)qc * L::QT + qw0 + jj;
+    const char* qsrc =
+        (const char*)a.q + ((cu * m.n_total + frame) * a.g.hq + g) * (long long)(L::D * 2);
+    uint4 qraw[4];
+    if (nqw > 0) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qraw[s] = gld<uint4>(qsrc + 32 * s + 16 * hf);
+    }
+#pragma unroll
+    for (int st = 0; st < L::NST - 1; ++st)
+        if (st < ntt) issue(st, st);
+
+    // rotate: the lane holds dims 16s + 8hf + e (s = 0..3, e = 0..7); NEOX
+    // pairs (i, i + 32) are chunks s and s + 2 of the same lane.
+    bf16x8_t qt[4];
+    if (nqw > 0) {
+        float cs[16], sn[16];
+        const double pd = (double)pq;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                rope_angle_q(pd, a.g.omega[16 * s + 8 * hf + e], &cs[8 * s + e], &sn[8 * s + e]);
+        if (ntt > 1) wait_vm<L::LPW * 2>(); else wait_vm<L::LPW>();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint32_t* x0 = (const uint32_t*)&qraw[s];
+            const uint32_t* x1 = (const uint32_t*)&qraw[s + 2];
+            uint32_t y0[4], y1[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                float a0[2], a1[2], b0[2], b1[2];
+                a0[0] = bf_lo(x0[w]); a0[1] = bf_hi(x0[w]);
+                a1[0] = bf_lo(x1[w]); a1[1] = bf_hi(x1[w]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const float c = cs[8 * s + 2 * w + u], sv = sn[8 * s + 2 * w + u];
+                    b0[u] = __fmaf_rn(a0[u], c, -(a1[u] * sv));
+                    b1[u] = __fmaf_rn(a1[u], c, a0[u] * sv);
+                }
+                y0[w] = pack_bf16x2(b0[0], b0[1]);
+                y1[w] = pack_bf16x2(b1[0], b1[1]);
+            }
+            qt[s] = __builtin_bit_cast(bf16x8_t, make_uint4(y0[0], y0[1], y0[2], y0[3]));
+            qt[s + 2] = __builtin_bit_cast(bf16x8_t, make_uint4(y1[0], y1[1], y1[2], y1[3]));
+        }
+    }
+
+    // ---- bands relative to T0: the lane's query, and the wave's union /
+    // intersection (for skipping and for mask-free half-tiles)
+    const int rlo_q = (int)(max(avail, pq - W + 1) - T0), rhi_q = (int)(pq - T0);
+    const long long wq_first = pq0 + qw0, wq_last = pq0 + qw0 + max(nqw, 1) - 1;
+    const int blo = (int)(max(avail, wq_first - W + 1) - T0), bhi = (int)(wq_last - T0);
+    const int flo = (int)(max(avail, wq_last - W + 1) - T0), fhi = (int)(wq_first - T0);
+
+    f32x16_t o[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    float mrow = kSent, lpart = 0.f;
+    const float sc = a.scale_log2;
+
+    for (int T = 0; T < ntt; ++T) {
+        if (T + 1 < ntt) wait_vm<L::LPW>(); else wait_vm<0>();
+        __syncthreads();
+        if (T + L::NST - 1 < ntt) issue(T + L::NST - 1, (T + L::NST - 1) % L::NST);
+        const char* Ks = lds + (T % L::NST) * 2 * L::TILE;
+        const char* Vs = Ks + L::TILE;
+        const int tb = T * kTile;
+        if (nqw <= 0 || tb + 63 < blo || tb > bhi) continue;   // no key of this tile for the wave
+        bool rel[2], full[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int kb = tb + 32 * k;
+            rel[k] = kb + 31 >= blo && kb <= bhi;
+            full[k] = kb >= flo && kb + 31 <= fhi;
+        }
+        f32x16_t s[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (!rel[k]) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[k][r] = 0.f;
+            const int row = 32 * k + jq;
+            const char* kr = Ks + row * L::RB;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int ch = (2 * st + hf) ^ ksw<L::CPR>(row);
+                const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, *(const uint4*)(kr + 16 * ch));
+                s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qt[st], s[k], 0, 0, 0);
+            }
+        }
+        // scale, mask, tile maximum of the lane's query
+        float mt = kSent;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (!rel[k]) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = s[k][r] * sc;
+                if (!full[k]) {
+                    const int key = tb + 32 * k + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    v = (key >= rlo_q && key <= rhi_q) ? v : kSent;
+                }
+                s[k][r] = v;
+                mt = fmaxf(mt, v);
+            }
+        }
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                             false, false);
+            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mn = fmaxf(mrow, mt);
+        const float alpha = fast_exp2(mrow - mn);
+        mrow = mn;
+        float lsum = 0.f;
+        uint32_t pb[2][8];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (!rel[k]) continue;
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = fast_exp2(s[k][r] - mn);
+                if (!full[k]) {
+                    const int key = tb + 32 * k + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    p[r] = (key >= rlo_q && key <= rhi_q) ? p[r] : 0.f;
+                }
+                lsum += p[r];
+            }
+#pragma unroll
+            for (int w = 0; w < 8; ++w) pb[k][w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
+        }
+        lpart = __fmaf_rn(lpart, alpha, lsum);
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+        // O^T += V^T P^T, key groups in ascending order
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (!rel[k]) continue;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bf16x8_t pv = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(pb[k][4 * c], pb[k][4 * c + 1], pb[k][4 * c + 2], pb[k][4 * c + 3]));
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                    v4i16 part[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int row = 32 * k + 16 * c + 8 * u + 4 * hf + ((lane & 15) >> 2);
+                        const int byte = 2 * col;
+                        const int ch = (byte >> 4) ^ vsw<BF16T, L::CPR>(row);
+                        part[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (VRT_LDS v4i16*)(__UINTPTR_TYPE__)(Vs + row * L::RB + 16 * ch + (byte & 15)));
+                    }
+                    const v8i16 vv = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pv,
+                                                                   o[d], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: denominator = lower-half partial + upper-half partial
+    if (nqw <= 0) return;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart), __float_as_uint(lpart),
+                                                     false, false);
+    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (jq >= nqw) return;
+    char* dst = (char*)a.out + ((cu * m.n_total + frame) * a.g.hq + g) * (long long)(L::D * 2);
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            uint2 v;
+            v.x = pack_bf16x2(o[d][4 * q4] / l, o[d][4 * q4 + 1] / l);
+            v.y = pack_bf16x2(o[d][4 * q4 + 2] / l, o[d][4 * q4 + 3] / l);
+            gst<uint2>(dst + 2 * (32 * d + 8 * q4 + 4 * hf), v);
+        }
+}
+
 // ---------------------------------------------- K5b: split-K merge ----
 // One wave per (unit, q head), lane = output dim.  Splits are merged in
 // ascending absolute order; splits past the window were never written.
@@ -738,6 +1058,14 @@ hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t 
         else VRT_ATTN(false, false, false);
     });
 #undef VRT_ATTN
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t s) {
+    if (a.g.dtype != 1 || a.g.D != 64 || a.g.group != 1 || a.g.mod || a.n_splits != 1)
+        return hipErrorInvalidValue;
+    const long long blocks = (long long)a.m.n_states * a.m.nl * a.g.hkv * a.n_qchunks;
+    hipLaunchKernelGGL(k_attn_mfma, dim3((unsigned)blocks), dim3(256), 0, s, a, t);
     return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ import numpy as np
 import torch
 
 import sliding_window_cached_amd as vrt
+from synth import qkv
 
 DEV = torch.device("cuda:0")
 F32_TOL = 1e-5
@@ -88,3 +89,33 @@ class Pool:
     def close(self):
         for s in self.states:
             s.close()
+
+
+def run_feeds(pool, idx, layer0, nl, qd, kd, vd, sizes, hooks=None):
+    """Feed device sequences [S][nl][T][H][d] in chunks; returns outputs."""
+    T = qd.shape[2]
+    out = torch.empty_like(qd)
+    states = [pool.states[i] for i in idx]
+    t, i = 0, 0
+    while t < T:
+        m = min(sizes[i % len(sizes)], T - t)
+        if hooks and i in hooks:
+            hooks[i]()
+        qc, kc, vc = (x[:, :, t:t + m].contiguous() for x in (qd, kd, vd))
+        oc = torch.empty_like(qc)
+        vrt.enc_attn_feed(states, layer0, nl, qc, kc, vc, m, oc, stream())
+        out[:, :, t:t + m] = oc
+        t += m
+        i += 1
+    torch.cuda.synchronize()
+    return out
+
+
+def seqs(seed, S, L, T, H, d, scale, dtype):
+    q = np.empty((S, L, T, H, d), np.float32)
+    k, v = np.empty_like(q), np.empty_like(q)
+    for s in range(S):
+        for l in range(L):
+            q[s, l], k[s, l], v[s, l] = qkv(seed, s, l, T, H, H, d, scale,
+                                           "bf16" if dtype == vrt.BF16 else "f32")
+    return q, k, v

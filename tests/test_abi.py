@@ -81,12 +81,17 @@ def test_ring_advance_matches_oracle_model():
             assert nc == len(r.events) - before
 
 
-def test_attn_path_is_a_function_of_dtype_and_n():
+def test_attn_path_is_a_function_of_desc_and_n():
     f32, bf = vrt.enc_desc(dtype=vrt.F32), vrt.enc_desc(dtype=vrt.BF16)
-    for n in (1, 4, 16, 31, 32, 512):
+    for n in (1, 4, 16, 31, 32, 512, 15300):
         assert vrt.attn_path(f32, n) == 0
-        assert vrt.attn_path(bf, n) in (0, 1)
-    assert vrt.attn_path(bf, 4) == 0
+        assert vrt.attn_path(bf, n) == (1 if n >= 32 else 0)
+        assert vrt.attn_path(vrt.dec_desc(), n) == 0                  # GQA decoder
+        assert vrt.attn_path(vrt.enc_desc(head_dim=128), n) == 0
+    assert vrt.attn_path(bf, 0) == -1
+    bad = vrt.enc_desc()
+    bad.reserved = 3
+    assert vrt.attn_path(bad, 64) == -1
 
 
 # A 256-byte aligned fake address: valid for host bookkeeping, never touched,

@@ -12,40 +12,11 @@ from oracle import attention, rope
 from oracle.ring import EncRing
 from synth import qkv, offsets
 
-from gpu_util import (DEV, Pool, check_close, empty, host, say, stream, to_dev, rel_err)
+from gpu_util import (DEV, Pool, check_close, empty, host, run_feeds, say, seqs, stream, to_dev,
+                      rel_err)
 
 pytestmark = pytest.mark.gpu
 THETA = 1.0e6
-
-
-def run_feeds(pool, idx, layer0, nl, qd, kd, vd, sizes, hooks=None):
-    """Feed device sequences [S][nl][T][H][d] in chunks; returns outputs."""
-    T = qd.shape[2]
-    out = torch.empty_like(qd)
-    states = [pool.states[i] for i in idx]
-    t, i = 0, 0
-    while t < T:
-        m = min(sizes[i % len(sizes)], T - t)
-        if hooks and i in hooks:
-            hooks[i]()
-        qc, kc, vc = (x[:, :, t:t + m].contiguous() for x in (qd, kd, vd))
-        oc = torch.empty_like(qc)
-        vrt.enc_attn_feed(states, layer0, nl, qc, kc, vc, m, oc, stream())
-        out[:, :, t:t + m] = oc
-        t += m
-        i += 1
-    torch.cuda.synchronize()
-    return out
-
-
-def seqs(seed, S, L, T, H, d, scale, dtype):
-    q = np.empty((S, L, T, H, d), np.float32)
-    k, v = np.empty_like(q), np.empty_like(q)
-    for s in range(S):
-        for l in range(L):
-            q[s, l], k[s, l], v[s, l] = qkv(seed, s, l, T, H, H, d, scale,
-                                           "bf16" if dtype == vrt.BF16 else "f32")
-    return q, k, v
 
 
 def test_c0_fp32_chunked_offline_oracle_and_compaction():
