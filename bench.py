@@ -1,18 +1,28 @@
 #!/usr/bin/env python3
 """Throughput of streamed windowed-750 encoder attention on one MI355X.
 
-Default workload (``--config c2``): steady-state serving, 256 independent
-streams x 1 layer, 20 heads x 64, window 750, 1536-slot rings pre-filled to
-750 frames (untimed), bf16 inputs N(0,1)*0.5 drawn on the GPU from a seeded
-generator, absolute start positions uniform in [1e4, 1e6).  One step = one
-call of the library's feed entry point that pushes 4 new frames into every
-stream: ring compaction where due, RoPE + append, windowed attention.  All
-inputs of all timed steps are resident in HBM before the timed region.
+Configurations (--config):
 
-Prints one JSON line: frames/s over all streams, the roofline of the
-attention kernel (algorithmic bytes per launch / its per-launch time from
-HIP events on the launch stream) and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+c2 (default)  steady-state serving: 256 independent streams x 1 layer, 20
+              heads x 64, window 750, 1536-slot rings pre-filled to 750 frames
+              (untimed), bf16 inputs N(0,1)*0.5 drawn on the GPU from a seeded
+              generator, absolute start positions uniform in [1e4, 1e6).  One
+              step = one feed call that pushes 4 new frames into every stream:
+              ring compaction where due, RoPE + append, windowed attention
+              (one fused launch on the vector path).
+c3            catch-up: 1 stream x 32 layers, bf16 N(0,1), 15300 frames fed as
+              29 batches of 512 + one of 452 (the maximum batch), compactions
+              before batches 4..30.  One step = one batch through all 32
+              layers: compaction, RoPE + append, attention on the matrix
+              cores.  The sequence restarts (host-only reset) after its last
+              batch.
+
+All inputs of all timed steps are resident in HBM before the timed region.
+Prints one JSON line: frames/s over all streams (a frame counts once, after
+every layer of the configuration has processed it), the roofline of the
+attention kernel (algorithmic bytes or flops per launch / its per-launch time
+from HIP events recorded on the launch stream) and the fp64 CPU oracle timed
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -26,39 +36,74 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
+H, D, W, SLOTS = 20, 64, 750, 1536
+R = H * D
+METRIC = "encoder frames/s through cached window-750 attention (all streams); % HBM peak"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline_c2(streams: int, steps: int, n: int = 4):
-    """The fp64 oracle (streamed form, the method itself) on a bounded sample
-    of the steady-state workload: `streams` streams pre-filled to 750 frames
-    (not timed), then `steps` feeds of `n` frames each (timed)."""
-    import numpy as np
-    from oracle.stream import EncStream
-    from synth import qkv, offsets
+def attn_work(n_kv: int, n: int, elem: int = 2):
+    """Algorithmic bytes and flops of one unit's attention over a sub-batch of
+    n frames when the ring held n_kv rows before it: read the n new queries,
+    the keys and values of the union window (min(n_kv, W-1) old rows plus the
+    n new ones), write n outputs; 4*d flops per (query, visible key) per head."""
+    old = min(n_kv, W - 1)
+    nbytes = (n + 2 * (old + n) + n) * R * elem
+    visible = sum(min(W, n_kv + j + 1) for j in range(n))
+    return nbytes, 4 * D * H * visible
 
-    starts = offsets(2, streams, 10 ** 4, 10 ** 6)
-    T = 750 + steps * n
+
+def cpu_baseline(streams: int, layers_in_config: int, pre: int, steps: int, n: int, scale: float,
+                 starts, what: str):
+    """The fp64 oracle (streamed form, the method itself) on a bounded sample:
+    `streams` single-layer streams pre-filled with `pre` frames (not timed),
+    then `steps` feeds of `n` frames (timed).  The rate is divided by the
+    configuration's layer count, so it is in the same unit as the GPU value
+    (frames through every layer)."""
+    from oracle.stream import EncStream
+    from synth import qkv
+
+    T = pre + steps * n
     elapsed = 0.0
     for s in range(streams):
-        q, k, v = qkv(2, s, 0, T, 20, 20, 64, 0.5, "bf16")
-        st = EncStream(20, 64, start_pos=int(starts[s]))
-        st.feed(q[:750], k[:750], v[:750])
+        q, k, v = qkv(2, s, 0, T, H, H, D, scale, "bf16")
+        st = EncStream(H, D, start_pos=int(starts[s]))
+        if pre:
+            st.feed(q[:pre], k[:pre], v[:pre])
         t0 = time.perf_counter()
         for i in range(steps):
-            a = 750 + i * n
+            a = pre + i * n
             st.feed(q[a:a + n], k[a:a + n], v[a:a + n])
         elapsed += time.perf_counter() - t0
-    frames = streams * steps * n
-    return {"value": frames / elapsed, "unit": "frames/s", "cores": 1, "kind": "oracle",
-            "sample": f"{streams} streams x {steps} steps x {n} frames of the same workload "
-                      f"(synthetic bf16 N(0,1)*0.5, rings pre-filled to 750, not timed), "
-                      f"oracle.stream.EncStream in fp64 numpy, one thread; "
-                      f"{elapsed:.1f} s for {frames} frames"}
+    frame_layers = streams * steps * n
+    return {"value": frame_layers / elapsed / layers_in_config, "unit": "frames/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{what}: {streams} stream(s) x 1 layer x {steps} feeds of {n} frames "
+                      f"(rings pre-filled with {pre} frames, not timed), oracle.stream.EncStream "
+                      f"in fp64 numpy on one thread, {elapsed:.1f} s for {frame_layers} "
+                      f"frame-layers, divided by {layers_in_config} layer(s) per frame"}
+
+
+def _randn(gen, shape, scale, dev):
+    import torch
+    x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    return (x * scale).to(torch.bfloat16)
+
+
+def _timing_events(n):
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:    # create the underlying events now (handles are lazy)
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    return evs
 
 
 def bench_c2(args):
@@ -67,8 +112,7 @@ def bench_c2(args):
     from synth import offsets
 
     dev = torch.device("cuda:0")
-    S, H, D, W, n = 256, 20, 64, 750, 4
-    R = H * D
+    S, n = 256, 4
     desc = vrt.enc_desc(dtype=vrt.BF16, n_layers=1)
     starts = offsets(2, S, 10 ** 4, 10 ** 6)
     nb = vrt.state_device_bytes(desc)
@@ -78,62 +122,53 @@ def bench_c2(args):
     gen = torch.Generator(device=dev)
     gen.manual_seed(2)
 
-    def randn(shape):
-        x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
-        return (x * 0.5).to(torch.bfloat16)
-
     log("c2: pre-filling 256 rings to 750 frames")
-    pre = [randn((S, 1, W, H, D)) for _ in range(3)]
+    pre = [_randn(gen, (S, 1, W, H, D), 0.5, dev) for _ in range(3)]
     pre_out = torch.empty_like(pre[0])
     vrt.enc_attn_feed(states, 0, 1, pre[0], pre[1], pre[2], W, pre_out, stream)
     torch.cuda.synchronize()
     del pre, pre_out
     total = args.warmup + args.steps
     log(f"c2: drawing inputs for {total} steps into HBM")
-    Q, K, V = (randn((total, S, 1, n, H, D)) for _ in range(3))
+    Q, K, V = (_randn(gen, (total, S, 1, n, H, D), 0.5, dev) for _ in range(3))
     out = torch.empty((S, 1, n, H, D), dtype=torch.bfloat16, device=dev)
 
     for i in range(args.warmup):
         vrt.enc_attn_feed(states, 0, 1, Q[i], K[i], V[i], n, out, stream)
     torch.cuda.synchronize()
 
-    # which timed steps compact (all rings share one schedule here)
-    base0, nkv0 = states[0].query(0)
-    compacting, nkv = [], nkv0
+    # which timed steps compact (all rings share one schedule here) and the
+    # ring occupancy each step's attention sees
+    _, nkv = states[0].query(0)
+    compacting, nkv_seen = [], []
     for i in range(args.steps):
-        _, nkv, nc = vrt.ring_advance(desc, 0, nkv, n)
+        _, nkv_after, nc = vrt.ring_advance(desc, 0, nkv, n)
         compacting.append(nc > 0)
+        nkv_seen.append(nkv_after - n)
+        nkv = nkv_after
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = _timing_events(args.steps)
     log(f"c2: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
         i = args.warmup + j
-        ev[j][0].record()
+        vrt.set_attn_events(ev[j][0], ev[j][1])
         vrt.enc_attn_feed(states, 0, 1, Q[i], K[i], V[i], n, out, stream)
-        ev[j][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev[0][0].elapsed_time(ev[-1][1])
-    per_step = [a.elapsed_time(b) for a, b in ev]
-    plain = [t for t, c in zip(per_step, compacting) if not c]
-    comp = [t for t, c in zip(per_step, compacting) if c]
+    vrt.set_attn_events()
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
     for s in states:
         s.close()
 
     frames = args.steps * S * n
-    value = frames / wall
-    # algorithmic bytes of one fused attention launch (every unit holds >= 749
-    # old frames): read q, k, v of the new frames (3n rows), write K/V rows
-    # (2n), read the 749 old K/V rows of the window (2*749), write out (n)
-    alg_bytes = S * (3 * n + 2 * n + 2 * 749 + n) * R * 2
-    t_kernel = sum(plain) / len(plain) * 1e-3
-    achieved = alg_bytes / t_kernel / 1e9
-    res = {
-        "metric": "encoder frames/s through cached window-750 attention (all streams); % HBM peak",
-        "value": value,
+    nbytes = [S * attn_work(k, n)[0] for k in nkv_seen]
+    t_kernel = sum(attn_ms) * 1e-3 / len(attn_ms)
+    achieved = sum(nbytes) / (sum(attn_ms) * 1e-3) / 1e9
+    return {
+        "metric": METRIC,
+        "value": frames / wall,
         "unit": "frames/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -146,51 +181,171 @@ def bench_c2(args):
         "data": "synthetic",
         "config": {
             "workload": "steady-state serving: 256 streams x 1 layer, 20 heads x 64, window 750, "
-                        "1536-slot ring pre-filled to 750, 4 frames per stream per step, bf16, "
-                        "start positions U[1e4, 1e6)",
+                        "1536-slot ring pre-filled to 750, 4 frames per stream per step, bf16 "
+                        "N(0,1)*0.5, start positions U[1e4, 1e6)",
             "streams": S, "layers": 1, "frames_per_step": n, "heads": H, "head_dim": D,
-            "window": W, "ring_slots": 1536, "parallelism": "none (1 GPU)",
+            "window": W, "ring_slots": SLOTS, "parallelism": "none (1 GPU)",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_attn_valu (fused RoPE+append+attention)",
+            "kernel": "k_attn (vector path: fused RoPE + append + attention, one launch per step)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": None,
-            "alg_bytes_per_launch": alg_bytes,
+            "alg_bytes_per_launch": nbytes[-1],
             "launch_us_mean": t_kernel * 1e6,
-            "launches_timed": len(plain),
+            "launches_timed": len(attn_ms),
         },
-        "gpu_ms_events": gpu_ms,
-        "compaction_step_us_mean": (sum(comp) / len(comp) * 1e3) if comp else None,
-        "step_hbm_frac": alg_bytes * args.steps / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "compaction_steps": sum(compacting),
+        "step_hbm_frac": sum(nbytes) / wall / 1e9 / HBM_PEAK_GBS,
     }
-    return res
+
+
+def c3_schedule(T=15300, B=512):
+    return [min(B, T - t) for t in range(0, T, B)]
+
+
+def bench_c3(args):
+    import torch
+    import sliding_window_cached_amd as vrt
+
+    dev = torch.device("cuda:0")
+    L, start = 32, 0
+    sched = c3_schedule()
+    desc = vrt.enc_desc(dtype=vrt.BF16, n_layers=L)
+    nb = vrt.state_device_bytes(desc)
+    mem = torch.empty(nb, dtype=torch.uint8, device=dev)
+    st = vrt.StreamState(desc, mem, nb, start)
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    log(f"c3: drawing 32 layers x {sum(sched)} frames into HBM ({len(sched)} batches)")
+    batches = [tuple(_randn(gen, (1, L, m, H, D), 1.0, dev) for _ in range(3)) for m in sched]
+    outs = {m: torch.empty((1, L, m, H, D), dtype=torch.bfloat16, device=dev) for m in set(sched)}
+
+    def feed(b):
+        q, k, v = batches[b]
+        vrt.enc_attn_feed([st], 0, L, q, k, v, sched[b], outs[sched[b]], stream)
+
+    # warmup: whole sequences from a reset ring
+    b = 0
+    for _ in range(args.warmup):
+        feed(b)
+        b += 1
+        if b == len(sched):
+            b = 0
+            st.reset(start)
+    torch.cuda.synchronize()
+
+    # host mirror of the ring each timed batch's attention sees
+    plan = []
+    bb, base, nkv = b, *st.query(0)
+    for j in range(args.steps):
+        m = sched[bb]
+        base, nkv_after, _ = vrt.ring_advance(desc, base, nkv, m)
+        plan.append((bb, m, nkv_after - m))
+        nkv = nkv_after
+        bb += 1
+        if bb == len(sched):
+            bb, base, nkv = 0, start, 0
+
+    ev = _timing_events(args.steps)
+    log(f"c3: timing {args.steps} batches")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j, (bj, m, _) in enumerate(plan):
+        vrt.set_attn_events(ev[j][0], ev[j][1])
+        feed(bj)
+        if bj == len(sched) - 1:
+            st.reset(start)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    vrt.set_attn_events()
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    st.close()
+
+    frames = sum(m for _, m, _ in plan)
+    work = [attn_work(k, m) for _, m, k in plan]
+    nbytes = sum(L * w[0] for w in work)
+    flops = sum(L * w[1] for w in work)
+    t_attn = sum(attn_ms) * 1e-3
+    tflops = flops / t_attn / 1e12
+    gbs = nbytes / t_attn / 1e9
+    full = [(a, L * attn_work(k, m)[1]) for a, (_, m, k) in zip(attn_ms, plan) if m == 512 and k >= W]
+    return {
+        "metric": METRIC,
+        "value": frames / wall,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "catch-up: 1 stream x 32 layers, 20 heads x 64, window 750, ring 1536, "
+                        "15300 frames as 29 x 512 + 452 (max batch 512), compactions between "
+                        "batches, bf16 N(0,1); one step = one batch through all 32 layers",
+            "streams": 1, "layers": L, "frames": sum(sched), "max_batch": 512, "heads": H,
+            "head_dim": D, "window": W, "ring_slots": SLOTS, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_attn_mfma (matrix path: S^T = K Q^T and O^T += V^T P^T on "
+                      "v_mfma_f32_32x32x16_bf16)",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFS,
+            "traffic": None,
+            "alg_flops_per_launch_full_window": full[0][1] if full else None,
+            "launch_us_mean": t_attn / len(attn_ms) * 1e6,
+            "launch_us_mean_full_window": (sum(a for a, _ in full) / len(full) * 1e3) if full else None,
+            "launches_timed": len(attn_ms),
+            "hbm_achieved_gbs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS,
+            "note": "algorithmic flops = 4*d*H per (query, visible key); the kernel is "
+                    "HBM-bound at the roofline (about 216 flop/B < the 312 flop/B ridge)",
+        },
+    }
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c2"])
+    ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
+    ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
+    ap.add_argument("--config", default="c2", choices=["c2", "c3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-streams", type=int, default=1)
-    ap.add_argument("--cpu-steps", type=int, default=400)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: streams are independent and would shard across "
               "GPUs with no exchange, but this build runs and reports a single GPU.",
               file=sys.stderr)
         sys.exit(2)
-    res = bench_c2(args)
-    if not args.no_cpu_baseline:
-        log("cpu baseline: timing the fp64 oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline_c2(args.cpu_streams, args.cpu_steps)
+    if args.config == "c2":
+        args.steps = 1000 if args.steps is None else args.steps
+        args.warmup = 20 if args.warmup is None else args.warmup
+        res = bench_c2(args)
     else:
+        args.steps = 300 if args.steps is None else args.steps
+        args.warmup = 30 if args.warmup is None else args.warmup
+        res = bench_c3(args)
+    if args.no_cpu_baseline:
         res["cpu_baseline"] = None
+    else:
+        log("cpu baseline: timing the fp64 oracle on a bounded sample")
+        from synth import offsets
+        if args.config == "c2":
+            res["cpu_baseline"] = cpu_baseline(1, 1, W, 400, 4, 0.5, offsets(2, 1, 10 ** 4, 10 ** 6),
+                                               "steady-state sample")
+        else:
+            res["cpu_baseline"] = cpu_baseline(1, 32, 0, 4, 512, 1.0, [0], "catch-up sample")
     print(json.dumps(res), flush=True)
 
 

@@ -26,7 +26,8 @@
  * Conventions for every entry point
  * ---------------------------------
  * - All device pointers are caller-owned; the library never allocates or
- *   frees device memory and holds no global state.  All device work is
+ *   frees device memory and holds no global state (apart from the optional
+ *   per-thread timing events of vrt_set_attn_events).  All device work is
  *   enqueued on the caller's `stream` and is asynchronous.
  * - Arguments are checked before anything is enqueued.  On any error nothing
  *   is enqueued and no state changes (streaming-plan page, "Per-hook
@@ -214,6 +215,20 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* states, int n_states, int 
                              int n_layers, const void* q, const void* k, const void* v,
                              int n_tok, void* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
+
+/* Per-component timing (the pages time each stage of a streamed feed on its
+ * own: family doc, Capability Validation table, Streaming row, items 7 and
+ * 8).  While both events are non-null, every later call on this thread
+ * records `start` on its stream just before each attention launch (after the
+ * compaction and append launches of the same sub-batch) and `stop` just
+ * after it (for the decode step, after the merge launch), so
+ * hipEventElapsedTime(start, stop) covers the attention kernels alone; a
+ * call with several attention launches leaves the pair on its last one.
+ * Events are caller-owned hipEvent_t handles created with timing enabled;
+ * passing two nulls turns recording off.  This per-thread pair is the only
+ * setting the library keeps.  VRT_ERR_INVALID if exactly one is null or a
+ * handle is not a valid event. */
+vrt_status vrt_set_attn_events(hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ EXPORTS = (
     "vrt_ring_offset", "vrt_stream_state_create", "vrt_stream_state_reset",
     "vrt_stream_state_destroy", "vrt_stream_state_query", "vrt_ring_advance", "vrt_attn_path",
     "vrt_offline_scratch_bytes", "vrt_enc_attn_offline", "vrt_enc_attn_feed",
-    "vrt_ring_compact", "vrt_dec_workspace_bytes", "vrt_dec_attn_step",
+    "vrt_ring_compact", "vrt_dec_workspace_bytes", "vrt_dec_attn_step", "vrt_set_attn_events",
 )
 
 
@@ -117,6 +117,7 @@ def _load():
         "vrt_dec_workspace_bytes": (c_size_t, [POINTER(CacheDesc), c_int, c_int, c_int]),
         "vrt_dec_attn_step": (c_int, [POINTER(P), c_int, c_int, c_int, P, P, P, c_int, P, P,
                                       c_size_t, P]),
+        "vrt_set_attn_events": (c_int, [P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -248,3 +249,14 @@ def dec_attn_step(states, layer0, n_layers, q, k, v, n_tok, out, workspace=None,
     if check:
         _check(s, "dec_attn_step")
     return s
+
+
+def set_attn_events(start=None, stop=None):
+    """Record `start` / `stop` around every later attention launch of this
+    thread (torch.cuda.Event objects that have been recorded once, or raw
+    hipEvent_t ints); no arguments turns recording off."""
+    def h(e):
+        if e is None:
+            return None
+        return e if isinstance(e, int) else e.cuda_event
+    _check(lib.vrt_set_attn_events(h(start), h(stop)), "set_attn_events")

@@ -25,6 +25,9 @@ COMMON = [
 DEVICE = [
     f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the softmax works on the
+    # score tiles in place instead of copying them out of AGPRs every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

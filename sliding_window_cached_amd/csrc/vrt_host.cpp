@@ -39,6 +39,18 @@ hipError_t note(hipError_t e) {
     return e;
 }
 
+// Optional timing events recorded around attention launches
+// (vrt_set_attn_events); null when off.
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+hipError_t record_start(hipStream_t s) {
+    return g_ev_start ? hipEventRecord(g_ev_start, s) : hipSuccess;
+}
+hipError_t record_stop(hipStream_t s) {
+    return g_ev_stop ? hipEventRecord(g_ev_stop, s) : hipSuccess;
+}
+
 // A HIP error code is sticky per thread: an earlier failed runtime call made
 // by someone else would otherwise be reported after our own launch.  Clear it
 // once before a call enqueues anything.
@@ -154,7 +166,10 @@ void attn_shape(const Geom& g, bool mfma, long long units, int n, AttnArgs* at) 
 }
 
 hipError_t launch_attn(const AttnArgs& at, bool mfma, const StateTable& t, hipStream_t s) {
-    return mfma ? launch_attn_mfma(at, t, s) : launch_attn_valu(at, t, s);
+    hipError_t e = record_start(s);
+    if (e == hipSuccess) e = mfma ? launch_attn_mfma(at, t, s) : launch_attn_valu(at, t, s);
+    if (e == hipSuccess) e = record_stop(s);
+    return e;
 }
 
 // Common checks for the batched calls.  Pure: touches nothing.
@@ -587,8 +602,10 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int laye
                             at.n_qchunks, at.n_splits);
             hipError_t err = hipSuccess;
             if (!at.append) err = note(launch_rope_append(aa, t, stream));
+            if (err == hipSuccess) err = note(record_start(stream));
             if (err == hipSuccess) err = note(launch_attn_valu(at, t, stream));
             if (err == hipSuccess && m == 1) err = note(launch_dec_combine(at, t, stream));
+            if (err == hipSuccess) err = note(record_stop(stream));
             if (err != hipSuccess) {
                 poison(st, n_states);
                 return VRT_ERR_DEVICE;
@@ -598,6 +615,23 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int laye
             for (int l = layer0; l < layer0 + n_layers; ++l) st[i]->n_kv[l] += m;
         t0 += m;
     }
+    return VRT_OK;
+}
+
+vrt_status vrt_set_attn_events(hipEvent_t start, hipEvent_t stop) {
+    if ((start == nullptr) != (stop == nullptr)) return VRT_ERR_INVALID;
+    if (start) {
+        for (hipEvent_t e : {start, stop}) {
+            const hipError_t q = hipEventQuery(e);
+            if (q != hipSuccess && q != hipErrorNotReady) {
+                note(q);
+                clear_sticky_error();
+                return VRT_ERR_INVALID;
+            }
+        }
+    }
+    g_ev_start = start;
+    g_ev_stop = stop;
     return VRT_OK;
 }
 

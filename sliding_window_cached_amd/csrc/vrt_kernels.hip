@@ -670,15 +670,20 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
 // Keys stream through LDS in 64-key tiles aligned to absolute position (the
 // same tiles and clamped-row fetch as the VALU kernel); a 32-key half-tile
 // outside the band of all 32 queries of a wave is skipped, which is exact:
-// such a half-tile would only add zero weights.  Every per-query step (the
-// two MFMA chains, the running max, the per-lane partial sums, the rescale)
-// depends only on that query's own window and the absolute tile grid, so the
-// result does not depend on how frames were batched.
+// such a half-tile would only add zero weights.  The softmax scale is folded
+// into the rotated query, so scores come out in log2 units, and the matrix
+// cores also subtract a per-query reference maximum (an extra k-step), which
+// moves only when a tile exceeds it by more than 2^8 (then the accumulators
+// are rescaled), so most tiles need neither a subtraction nor a rescale on
+// the vector ALU.  The denominator sums the bf16 weights the products use.
+// Every per-query step (the MFMA chains, the reference, the partial sums,
+// the rescale) depends only on that query's own window and the absolute tile
+// grid, so the result does not depend on how frames were batched.
 //
 // Queries are rotated in the prologue: the angle p * omega_i is formed and
 // reduced by 2 pi in fp64 as for the keys, then sin and cos are taken in fp32
 // on the reduced angle (error ~3e-7 rad, far below the bf16 rounding of the
-// rotated query that follows).
+// rotated, scaled query that follows).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -696,21 +701,35 @@ struct M4 {
     static constexpr int BYTES = NST * 2 * TILE;
 };
 static_assert(M4::QT == kQTileMfma, "query tile of the MFMA path");
+// A query's reference maximum moves only when a tile exceeds it by more than
+// this (log2 units), so unnormalised weights stay below 2^8.
+constexpr float kLazy = 8.0f;
 
-__device__ __forceinline__ void rope_angle_q(double pos, double omega, float* c, float* s) {
-    double x = pos * omega;
-    if (fabs(x) < 2.6e7) {
-        const double k = rint(x * 0.15915494309189535);
-        x = fma(-k, 6.283185303211212, x);
-        x = fma(-k, 3.9683743166540886e-09, x);
-        x = fma(-k, 2.068073192717642e-18, x);
-        sincosf((float)x, s, c);
-    } else {
-        double sd, cd;
-        sincos(x, &sd, &cd);
-        *s = (float)sd;
-        *c = (float)cd;
-    }
+// (cos, sin) of a query rotation angle.  Near form: the fp64 angle is reduced
+// by 2 pi with the three-part Cody-Waite constants (valid while |x| < 2.6e7)
+// and the hardware sine / cosine run on the reduced angle in revolutions.
+// Far form (positions past ~2.6e7): fp64 library sin / cos, out of line.
+struct CosSin { float c, s; };
+// A wave-uniform double kept in scalar registers (so that a per-lane choice
+// between two of them selects values, not addresses to load from).
+__device__ __forceinline__ double uniform(double v) {
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ CosSin rope_cs_near(double x) {
+    const double k = rint(x * 0.15915494309189535);
+    x = fma(-k, 6.283185303211212, x);
+    x = fma(-k, 3.9683743166540886e-09, x);
+    x = fma(-k, 2.068073192717642e-18, x);
+    const float r = (float)(x * 0.15915494309189535);
+    return CosSin{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
+}
+__device__ __attribute__((noinline)) CosSin rope_cs_far(double x) {
+    double sd, cd;
+    sincos(x, &sd, &cd);
+    return CosSin{(float)cd, (float)sd};
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -797,14 +816,35 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
     // rotate: the lane holds dims 16s + 8hf + e (s = 0..3, e = 0..7); NEOX
     // pairs (i, i + 32) are chunks s and s + 2 of the same lane.
     bf16x8_t qt[4];
+    const float qscale = a.scale_log2;   // scores come out in log2 units
     if (nqw > 0) {
         float cs[16], sn[16];
         const double pd = (double)pq;
+        // frequency 16s + 8hf + e: both halves' values are uniform, so they
+        // come from the scalar argument block and are selected per lane
+        double om[16];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                rope_angle_q(pd, a.g.omega[16 * s + 8 * hf + e], &cs[8 * s + e], &sn[8 * s + e]);
+                om[8 * s + e] = hf ? uniform(a.g.omega[16 * s + 8 + e]) : uniform(a.g.omega[16 * s + e]);
+        // omega_0 = 1 is the largest frequency
+        if (__builtin_amdgcn_ballot_w64(fabs(pd * a.g.omega[0]) >= 2.6e7) == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const CosSin r = rope_cs_near(pd * om[i]);
+                cs[i] = r.c;
+                sn[i] = r.s;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const double x = pd * om[i];
+                const CosSin r = fabs(x) < 2.6e7 ? rope_cs_near(x) : rope_cs_far(x);
+                cs[i] = r.c;
+                sn[i] = r.s;
+            }
+        }
         if (ntt > 1) wait_vm<L::LPW * 2>(); else wait_vm<L::LPW>();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -819,8 +859,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const float c = cs[8 * s + 2 * w + u], sv = sn[8 * s + 2 * w + u];
-                    b0[u] = __fmaf_rn(a0[u], c, -(a1[u] * sv));
-                    b1[u] = __fmaf_rn(a1[u], c, a0[u] * sv);
+                    b0[u] = __fmaf_rn(a0[u], c, -(a1[u] * sv)) * qscale;
+                    b1[u] = __fmaf_rn(a1[u], c, a0[u] * sv) * qscale;
                 }
                 y0[w] = pack_bf16x2(b0[0], b0[1]);
                 y1[w] = pack_bf16x2(b1[0], b1[1]);
@@ -842,8 +882,20 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
     for (int d = 0; d < 2; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-    float mrow = kSent, lpart = 0.f;
-    const float sc = a.scale_log2;
+    // Reference maximum of the lane's query (log2 units), subtracted from the
+    // scores by the matrix cores themselves: a fifth k-step per score block
+    // multiplies the constant operand kext (ones at k = 0, 1) with qext =
+    // (-m_hi, -m_lo), the reference split into two bf16 values, so the block
+    // comes out as s - mref with mref = m_hi + m_lo exactly.  mref is 0 until
+    // the query's first visible key, then moves only when a tile's maximum
+    // exceeds it by more than kLazy (weights stay below 2^kLazy); a lane whose
+    // reference does not move is rescaled by exactly 1, if at all.
+    const uint32_t one_lo = hf == 0 ? 0x3f803f80u : 0u;
+    const bf16x8_t kext = __builtin_bit_cast(bf16x8_t, make_uint4(one_lo, 0u, 0u, 0u));
+    bf16x8_t qext = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+    float mref = 0.f, lpart = 0.f;
+    bool seen = false;
+    constexpr uint32_t kOnes = 0x3f803f80u;   // (1, 1) in bf16
 
     for (int T = 0; T < ntt; ++T) {
         if (T + 1 < ntt) wait_vm<L::LPW>(); else wait_vm<0>();
@@ -860,68 +912,88 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
             rel[k] = kb + 31 >= blo && kb <= bhi;
             full[k] = kb >= flo && kb + 31 <= fhi;
         }
+        // scores relative to the reference: S^T = [K | 1] [Q | -mref]^T
         f32x16_t s[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             if (!rel[k]) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[k][r] = 0.f;
             const int row = 32 * k + jq;
             const char* kr = Ks + row * L::RB;
+            bf16x8_t kv[4];
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int ch = (2 * st + hf) ^ ksw<L::CPR>(row);
-                const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, *(const uint4*)(kr + 16 * ch));
-                s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qt[st], s[k], 0, 0, 0);
-            }
+            for (int st = 0; st < 4; ++st)
+                kv[st] = __builtin_bit_cast(
+                    bf16x8_t, *(const uint4*)(kr + 16 * ((2 * st + hf) ^ ksw<L::CPR>(row))));
+            s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, f32x16_t{}, 0, 0, 0);
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[st], qt[st], s[k], 0, 0, 0);
         }
-        // scale, mask, tile maximum of the lane's query
+        // mask (edge half-tiles only; masked scores become the sentinel, whose
+        // weight underflows to exactly 0) and the tile maximum
         float mt = kSent;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             if (!rel[k]) continue;
+            if (!full[k]) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float v = s[k][r] * sc;
-                if (!full[k]) {
+                for (int r = 0; r < 16; ++r) {
                     const int key = tb + 32 * k + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    v = (key >= rlo_q && key <= rhi_q) ? v : kSent;
+                    s[k][r] = (key >= rlo_q && key <= rhi_q) ? s[k][r] : kSent;
                 }
-                s[k][r] = v;
-                mt = fmaxf(mt, v);
             }
+#pragma unroll
+            for (int r = 0; r < 16; r += 4)
+                mt = fmaxf(fmaxf(mt, fmaxf(s[k][r], s[k][r + 1])), fmaxf(s[k][r + 2], s[k][r + 3]));
         }
         {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                              false, false);
             mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        const float mn = fmaxf(mrow, mt);
-        const float alpha = fast_exp2(mrow - mn);
-        mrow = mn;
-        float lsum = 0.f;
+        const bool move = seen ? mt > kLazy : mt > kSent;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {   // a query's first keys, or a jump of 2^kLazy
+            float delta = 0.f;
+            if (move) {
+                const float mnew = mref + mt;
+                const uint32_t hi = to_bf16(mnew);
+                const float mhi = __uint_as_float(hi << 16);
+                const uint32_t lo = to_bf16(mnew - mhi);
+                const float mt_ref = mhi + __uint_as_float(lo << 16);
+                const float alpha = seen ? fast_exp2(mref - mt_ref) : 0.f;
+                lpart *= alpha;
+#pragma unroll
+                for (int d = 0; d < 2; ++d)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+                delta = mt_ref - mref;
+                mref = mt_ref;
+                seen = true;
+                const uint32_t neg = (hi ^ 0x8000u) | ((lo ^ 0x8000u) << 16);
+                qext = __builtin_bit_cast(bf16x8_t, make_uint4(hf == 0 ? neg : 0u, 0u, 0u, 0u));
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                if (!rel[k]) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[k][r] -= delta;
+            }
+        }
         uint32_t pb[2][8];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             if (!rel[k]) continue;
-            float p[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = fast_exp2(s[k][r] - mn);
-                if (!full[k]) {
-                    const int key = tb + 32 * k + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    p[r] = (key >= rlo_q && key <= rhi_q) ? p[r] : 0.f;
-                }
-                lsum += p[r];
-            }
-#pragma unroll
-            for (int w = 0; w < 8; ++w) pb[k][w] = pack_bf16x2(p[2 * w], p[2 * w + 1]);
+            for (int w = 0; w < 8; ++w)
+                pb[k][w] = pack_bf16x2(fast_exp2(s[k][2 * w]), fast_exp2(s[k][2 * w + 1]));
         }
-        lpart = __fmaf_rn(lpart, alpha, lsum);
+        // the denominator sums the same bf16 weights the products use
 #pragma unroll
-        for (int d = 0; d < 2; ++d)
+        for (int k = 0; k < 2; ++k) {
+            if (!rel[k]) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+            for (int w = 0; w < 8; ++w) lpart = dot2bf(pb[k][w], kOnes, lpart);
+        }
         // O^T += V^T P^T, key groups in ascending order
 #pragma unroll
         for (int k = 0; k < 2; ++k) {

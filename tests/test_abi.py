@@ -162,6 +162,13 @@ def test_decoder_argument_errors():
     assert st.query(0) == (0, 0)
 
 
+def test_set_attn_events_argument_checks():
+    vrt.set_attn_events()                     # off: always accepted
+    assert vrt.lib.vrt_set_attn_events(FAKE, None) == vrt.ERR_INVALID
+    assert vrt.lib.vrt_set_attn_events(None, FAKE) == vrt.ERR_INVALID
+    vrt.set_attn_events()
+
+
 def test_single_hip_runtime_in_process():
     """libvrt and PyTorch must share one HIP runtime (a second runtime in the
     same process sees no GPU), whichever is imported first."""
