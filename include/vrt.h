@@ -38,7 +38,8 @@
  * - If a kernel launch reports an error, VRT_ERR_DEVICE is returned and every
  *   state in the call is marked poisoned; poisoned states refuse every call
  *   (VRT_ERR_POISONED) until vrt_stream_state_reset.
- * - Absolute positions are int64 and must stay in [0, 2^53).
+ * - Absolute positions are int64 and must stay in [0, 2^31): a call whose
+ *   frames would reach 2^31 fails with VRT_ERR_INVALID.
  * - Tensors are contiguous, row-major, in the state's dtype (float32 or
  *   bfloat16 bit patterns), 256-byte aligned device pointers.
  */

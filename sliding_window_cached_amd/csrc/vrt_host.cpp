@@ -26,7 +26,10 @@ namespace {
 
 using namespace vrt;
 
-constexpr int64_t kPosLimit = (int64_t)1 << 53;
+// Absolute positions stay below 2^31 (about 1.4 years of 50 Hz encoder
+// frames); the query rotation of the matrix path reduces its angles exactly
+// up to this bound.
+constexpr int64_t kPosLimit = (int64_t)1 << 31;
 
 // Text of the last HIP error a launch on this thread reported (diagnostics
 // only; read through vrt_last_device_error).

@@ -322,9 +322,28 @@ __device__ __forceinline__ int vsw(int r) {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define VRT_LDS __attribute__((address_space(3)))
 
+// 16 bytes per lane, HBM -> LDS (global_load_lds_dwordx4: lane i writes
+// bytes [16i, 16i + 16) after the wave-uniform LDS address in M0).  Issued
+// through inline asm on purpose: the compiler does not track LDS writes
+// made this way, so it does not make every later LDS read of the tile loop
+// wait for the DMA of the tile being prefetched.  Every read of a stage is
+// ordered after its DMA explicitly (wait_vm, then a workgroup barrier).
+// Untracked vector-memory operations can only make the compiler's own
+// vmcnt waits stricter, never weaker.
+// M0 is saved and restored around the instruction (the compiler reserves
+// it), with the one wait state an M0 write needs before an LDS DMA.
 __device__ __forceinline__ void dma16(const char* g, char* l) {
-    __builtin_amdgcn_global_load_lds((VRT_GLOBAL void*)(__UINTPTR_TYPE__)g,
-                                     (VRT_LDS void*)(__UINTPTR_TYPE__)l, 16, 0, 0);
+    const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(__UINTPTR_TYPE__)l);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"((unsigned long long)(__UINTPTR_TYPE__)g), "s"(lds)
+        : "memory");
 }
 // wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
@@ -705,31 +724,29 @@ static_assert(M4::QT == kQTileMfma, "query tile of the MFMA path");
 // this (log2 units), so unnormalised weights stay below 2^8.
 constexpr float kLazy = 8.0f;
 
-// (cos, sin) of a query rotation angle.  Near form: the fp64 angle is reduced
-// by 2 pi with the three-part Cody-Waite constants (valid while |x| < 2.6e7)
-// and the hardware sine / cosine run on the reduced angle in revolutions.
-// Far form (positions past ~2.6e7): fp64 library sin / cos, out of line.
+// (cos, sin) of a query rotation angle x = p * omega_i, 0 <= p < 2^31.  The
+// fp64 angle is reduced by 2 pi with a four-part Cody-Waite split whose first
+// three parts have 24 significant bits, so k * c_j is exact for |k| < 2^29
+// (every angle below 3.3e9 rad, which covers all positions the library
+// accepts) and the reduced angle is accurate to about 1e-15 rad; the
+// hardware sine / cosine then run on it in revolutions (1.2e-7 abs. error).
 struct CosSin { float c, s; };
-// A wave-uniform double kept in scalar registers (so that a per-lane choice
-// between two of them selects values, not addresses to load from).
-__device__ __forceinline__ double uniform(double v) {
-    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
-    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
-    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
-    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
-}
-__device__ __forceinline__ CosSin rope_cs_near(double x) {
-    const double k = rint(x * 0.15915494309189535);
-    x = fma(-k, 6.283185303211212, x);
-    x = fma(-k, 3.9683743166540886e-09, x);
-    x = fma(-k, 2.068073192717642e-18, x);
-    const float r = (float)(x * 0.15915494309189535);
+__device__ __forceinline__ CosSin rope_cs(double x) {
+    const double k = rint(x * 0x1.45f306dc9c883p-3);      // x / (2 pi)
+    x = fma(-k, 0x1.921fb60000000p+2, x);
+    x = fma(-k, -0x1.777a5c0000000p-23, x);
+    x = fma(-k, -0x1.ee59da0000000p-48, x);
+    x = fma(-k, 0x1.98a2e03707345p-75, x);
+    const float r = (float)(x * 0x1.45f306dc9c883p-3);
     return CosSin{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
 }
-__device__ __attribute__((noinline)) CosSin rope_cs_far(double x) {
-    double sd, cd;
-    sincos(x, &sd, &cd);
-    return CosSin{(float)cd, (float)sd};
+
+// max(a, b, c) in one instruction (operands are finite or the sentinel, so
+// no NaN handling is needed)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -805,9 +822,15 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
     const char* qsrc =
         (const char*)a.q + ((cu * m.n_total + frame) * a.g.hq + g) * (long long)(L::D * 2);
     uint4 qraw[4];
+    double om[16];
     if (nqw > 0) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) qraw[s] = gld<uint4>(qsrc + 32 * s + 16 * hf);
+        const double* wp = a.g.omega + 8 * hf;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) om[8 * s + e] = wp[16 * s + e];
     }
 #pragma unroll
     for (int st = 0; st < L::NST - 1; ++st)
@@ -820,30 +843,13 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
     if (nqw > 0) {
         float cs[16], sn[16];
         const double pd = (double)pq;
-        // frequency 16s + 8hf + e: both halves' values are uniform, so they
-        // come from the scalar argument block and are selected per lane
-        double om[16];
+        // frequencies 16s + 8hf + e: two contiguous runs of 8 doubles of
+        // the argument block per lane, loaded up front
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                om[8 * s + e] = hf ? uniform(a.g.omega[16 * s + 8 + e]) : uniform(a.g.omega[16 * s + e]);
-        // omega_0 = 1 is the largest frequency
-        if (__builtin_amdgcn_ballot_w64(fabs(pd * a.g.omega[0]) >= 2.6e7) == 0) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const CosSin r = rope_cs_near(pd * om[i]);
-                cs[i] = r.c;
-                sn[i] = r.s;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const double x = pd * om[i];
-                const CosSin r = fabs(x) < 2.6e7 ? rope_cs_near(x) : rope_cs_far(x);
-                cs[i] = r.c;
-                sn[i] = r.s;
-            }
+        for (int i = 0; i < 16; ++i) {
+            const CosSin r = rope_cs(pd * om[i]);
+            cs[i] = r.c;
+            sn[i] = r.s;
         }
         if (ntt > 1) wait_vm<L::LPW * 2>(); else wait_vm<L::LPW>();
 #pragma unroll
@@ -890,6 +896,17 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
     // the query's first visible key, then moves only when a tile's maximum
     // exceeds it by more than kLazy (weights stay below 2^kLazy); a lane whose
     // reference does not move is rescaled by exactly 1, if at all.
+    // lane parts of the LDS addresses (the swizzles depend only on lane
+    // bits, so each read is a stage base + one of these + an immediate)
+    int koff[4], voff[2];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) koff[st] = jq * L::RB + 16 * ((2 * st + hf) ^ ksw<L::CPR>(jq));
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const int row = 4 * hf + ((lane & 15) >> 2);
+        const int byte = 2 * (32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+        voff[d] = L::TILE + row * L::RB + 16 * ((byte >> 4) ^ vsw<BF16T, L::CPR>(row)) + (byte & 15);
+    }
     const uint32_t one_lo = hf == 0 ? 0x3f803f80u : 0u;
     const bf16x8_t kext = __builtin_bit_cast(bf16x8_t, make_uint4(one_lo, 0u, 0u, 0u));
     bf16x8_t qext = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
@@ -901,8 +918,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
         if (T + 1 < ntt) wait_vm<L::LPW>(); else wait_vm<0>();
         __syncthreads();
         if (T + L::NST - 1 < ntt) issue(T + L::NST - 1, (T + L::NST - 1) % L::NST);
-        const char* Ks = lds + (T % L::NST) * 2 * L::TILE;
-        const char* Vs = Ks + L::TILE;
+        const char* Sb = lds + (T % L::NST) * 2 * L::TILE;   // K tile, then V tile
         const int tb = T * kTile;
         if (nqw <= 0 || tb + 63 < blo || tb > bhi) continue;   // no key of this tile for the wave
         bool rel[2], full[2];
@@ -913,21 +929,33 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
             full[k] = kb >= flo && kb + 31 <= fhi;
         }
         // scores relative to the reference: S^T = [K | 1] [Q | -mref]^T
+        // both half-tiles' K operands first, then the two MFMA chains
+        // interleaved (each chain keeps its own k order)
         f32x16_t s[2];
+        bf16x8_t kv[2][4];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (!rel[k]) continue;
-            const int row = 32 * k + jq;
-            const char* kr = Ks + row * L::RB;
-            bf16x8_t kv[4];
+        for (int k = 0; k < 2; ++k)
 #pragma unroll
             for (int st = 0; st < 4; ++st)
-                kv[st] = __builtin_bit_cast(
-                    bf16x8_t, *(const uint4*)(kr + 16 * ((2 * st + hf) ^ ksw<L::CPR>(row))));
-            s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, f32x16_t{}, 0, 0, 0);
+                kv[k][st] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(Sb + koff[st] + 32 * k * L::RB));
+        if (rel[0] && rel[1]) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, f32x16_t{}, 0, 0, 0);
 #pragma unroll
             for (int st = 0; st < 4; ++st)
-                s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[st], qt[st], s[k], 0, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[k][st], qt[st], s[k], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                if (!rel[k]) continue;
+                s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, f32x16_t{}, 0, 0, 0);
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[k][st], qt[st], s[k], 0, 0, 0);
+            }
         }
         // mask (edge half-tiles only; masked scores become the sentinel, whose
         // weight underflows to exactly 0) and the tile maximum
@@ -943,13 +971,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 16; r += 4)
-                mt = fmaxf(fmaxf(mt, fmaxf(s[k][r], s[k][r + 1])), fmaxf(s[k][r + 2], s[k][r + 3]));
+            for (int r = 0; r < 16; r += 2) mt = max3f(mt, s[k][r], s[k][r + 1]);
         }
         {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                              false, false);
-            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            mt = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), kSent);
         }
         const bool move = seen ? mt > kLazy : mt > kSent;
         if (__builtin_amdgcn_ballot_w64(move) != 0) {   // a query's first keys, or a jump of 2^kLazy
@@ -1004,16 +1031,11 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
                     bf16x8_t, make_uint4(pb[k][4 * c], pb[k][4 * c + 1], pb[k][4 * c + 2], pb[k][4 * c + 3]));
 #pragma unroll
                 for (int d = 0; d < 2; ++d) {
-                    const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
                     v4i16 part[2];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int row = 32 * k + 16 * c + 8 * u + 4 * hf + ((lane & 15) >> 2);
-                        const int byte = 2 * col;
-                        const int ch = (byte >> 4) ^ vsw<BF16T, L::CPR>(row);
-                        part[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (VRT_LDS v4i16*)(__UINTPTR_TYPE__)(Vs + row * L::RB + 16 * ch + (byte & 15)));
-                    }
+                    for (int u = 0; u < 2; ++u)
+                        part[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VRT_LDS v4i16*)(__UINTPTR_TYPE__)(
+                            Sb + voff[d] + (32 * k + 16 * c + 8 * u) * L::RB));
                     const v8i16 vv = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
                     o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pv,
                                                                    o[d], 0, 0, 0);

@@ -162,6 +162,26 @@ def test_decoder_argument_errors():
     assert st.query(0) == (0, 0)
 
 
+def test_position_limit():
+    """Absolute positions stay below 2^31: creation at 2^31 and feeds whose
+    frames would reach it are refused before anything is enqueued."""
+    d = vrt.enc_desc()
+    lim = 2 ** 31
+    with pytest.raises(vrt.VrtError) as e:
+        _state(d, lim)
+    assert e.value.status == vrt.ERR_INVALID
+    st = _state(d, lim - 3)
+    P = FAKE
+    assert vrt.enc_attn_feed([st], 0, 1, P, P, P, 4, P, 0, check=False) == vrt.ERR_INVALID
+    assert st.query(0) == (lim - 3, 0)
+    sb = vrt.offline_scratch_bytes(d, 4)
+    assert vrt.lib.vrt_enc_attn_offline(ctypes.byref(d), P, P, P, 4, lim - 3, P, P, sb, None) \
+        == vrt.ERR_INVALID
+    dd = vrt.dec_desc()
+    ds = _state(dd, lim - 1)
+    assert vrt.dec_attn_step([ds], 0, 1, P, P, P, 2, P, check=False) == vrt.ERR_INVALID
+
+
 def test_set_attn_events_argument_checks():
     vrt.set_attn_events()                     # off: always accepted
     assert vrt.lib.vrt_set_attn_events(FAKE, None) == vrt.ERR_INVALID

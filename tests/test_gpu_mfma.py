@@ -92,13 +92,14 @@ def test_catchup_any_chunking_offline_and_oracle():
 def test_catchup_threshold_and_ragged_query_tiles():
     """Sub-batch sizes at the path threshold and around the 128-query tile
     (32, 33, 127, 128, 129, 130: tiles with 1 or 2 queries, waves with none),
-    from an empty ring at position 0 and at an unaligned large position:
+    from an empty ring at position 0, at an unaligned large position and
+    ending at the last position the library accepts (2^31 - 1):
     bit-identical to the offline pass; every row checked against the oracle."""
     H, d = 20, 64
     sizes = [32, 33, 127, 128, 129, 130, 64]
     T = sum(sizes) * 2
     desc = vrt.enc_desc(dtype=vrt.BF16, n_layers=1)
-    for start in (0, 987_655):
+    for start in (0, 987_655, 2 ** 31 - T):
         q, k, v = seqs(31, 1, 1, T, H, d, 1.0, vrt.BF16)
         qd, kd, vd = (to_dev(x, vrt.BF16) for x in (q, k, v))
         pool = Pool(desc, 1, [start])
