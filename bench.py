@@ -193,7 +193,7 @@ def bench_c2(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": (measured_traffic("k_attn", "c2") or {}).get("bytes"),
             "alg_bytes_per_launch": nbytes[-1],
             "launch_us_mean": t_kernel * 1e6,
             "launches_timed": len(attn_ms),
@@ -201,6 +201,52 @@ def bench_c2(args):
         "compaction_steps": sum(compacting),
         "step_hbm_frac": sum(nbytes) / wall / 1e9 / HBM_PEAK_GBS,
     }
+
+
+KERNEL_SRC = os.path.join(ROOT, "sliding_window_cached_amd", "csrc", "vrt_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def kernels_sha256() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs recorded in profiles/hbm_traffic.txt
+    (already scaled by the copy-kernel calibration there), or None when no
+    record exists or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = kernels_sha256()
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) == 5 and f[0] == kernel and f[1] == workload and f[4] == f"kernels_sha256={sha}":
+            return {"fetch_bytes": float(f[2]), "write_bytes": float(f[3]),
+                    "bytes": float(f[2]) + float(f[3])}
+    return None
+
+
+def bench_copy(args):
+    """Calibration: a plain device-to-device copy of 1 GiB, `steps` times
+    (reads and writes exactly 2^30 bytes per launch)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"metric": "device copy bandwidth (calibration)", "value": 2 * n * args.steps / wall / 1e9,
+            "unit": "GB/s", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+            "steps": args.steps}
 
 
 def c3_schedule(T=15300, B=512):
@@ -302,7 +348,7 @@ def bench_c3(args):
             "peak": MFMA_BF16_PEAK_TFS,
             "unit": "TFLOP/s",
             "frac": tflops / MFMA_BF16_PEAK_TFS,
-            "traffic": None,
+            "traffic": (measured_traffic("k_attn_mfma", "c3") or {}).get("bytes"),
             "alg_flops_per_launch_full_window": full[0][1] if full else None,
             "launch_us_mean": t_attn / len(attn_ms) * 1e6,
             "launch_us_mean_full_window": (sum(a for a, _ in full) / len(full) * 1e3) if full else None,
@@ -320,7 +366,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
-    ap.add_argument("--config", default="c2", choices=["c2", "c3"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -328,6 +374,11 @@ def main():
               "GPUs with no exchange, but this build runs and reports a single GPU.",
               file=sys.stderr)
         sys.exit(2)
+    if args.config == "copy":
+        args.steps = 20 if args.steps is None else args.steps
+        args.warmup = 2 if args.warmup is None else args.warmup
+        print(json.dumps(bench_copy(args)), flush=True)
+        return
     if args.config == "c2":
         args.steps = 1000 if args.steps is None else args.steps
         args.warmup = 20 if args.warmup is None else args.warmup
