@@ -1,6 +1,6 @@
 // gfx950 kernels for streamed windowed-causal attention.
 //
-//   k_rope_append  NEOX RoPE (theta^(-2i/d) frequencies, angle in fp64) of the
+//   k_rope_append  NEOX RoPE (theta^(-2i/d) frequencies, angle formed in fp64) of the
 //                  new keys, then the rotated keys and the raw values are
 //                  written to their ring slots (Voxtral Realtime streaming-plan
 //                  page, "SHIPPED" section: the chunk's K/V go to rows
@@ -120,6 +120,51 @@ __device__ __forceinline__ void rope_rot(float x0, float x1, double c, double s,
     *y1 = (float)(e + f);
 }
 
+// (cos, sin) of a rotation angle x = p * omega_i, 0 <= p < 2^31.  The
+// fp64 angle is reduced by 2 pi with a four-part Cody-Waite split whose first
+// three parts have 24 significant bits, so k * c_j is exact for |k| < 2^29
+// (every angle below 3.3e9 rad, which covers all positions the library
+// accepts) and the reduced angle is accurate to about 1e-15 rad; the
+// hardware sine / cosine then run on it in revolutions (1.2e-7 abs. error).
+struct CosSin { float c, s; };
+__device__ __forceinline__ CosSin rope_cs(double x) {
+    const double k = rint(x * 0x1.45f306dc9c883p-3);      // x / (2 pi)
+    x = fma(-k, 0x1.921fb60000000p+2, x);
+    x = fma(-k, -0x1.777a5c0000000p-23, x);
+    x = fma(-k, -0x1.ee59da0000000p-48, x);
+    x = fma(-k, 0x1.98a2e03707345p-75, x);
+    const float r = (float)(x * 0x1.45f306dc9c883p-3);
+    return CosSin{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
+}
+
+// One NEOX rotation per storage type.  fp32 storage: fp64 sin / cos and an
+// fp64 rotation rounded once to fp32 (rope_angle, rope_rot).  bf16 storage:
+// the exactly reduced angle and the hardware sine / cosine (rope_cs) and an
+// fp32 rotation; its error (~1e-7 of the values) is far below the bf16
+// rounding of the result.  Keys are written by one function per storage
+// type whichever kernel appends them, so ring contents do not depend on the
+// path that wrote them.
+template <class E> struct Angle;
+template <> struct Angle<F32T> { double c, s; };
+template <> struct Angle<BF16T> { float c, s; };
+template <class E> __device__ __forceinline__ Angle<E> rope_of(long long pos, double omega);
+template <> __device__ __forceinline__ Angle<F32T> rope_of<F32T>(long long pos, double omega) {
+    Angle<F32T> a;
+    rope_angle(pos, omega, &a.c, &a.s);
+    return a;
+}
+template <> __device__ __forceinline__ Angle<BF16T> rope_of<BF16T>(long long pos, double omega) {
+    const CosSin r = rope_cs((double)pos * omega);
+    return Angle<BF16T>{r.c, r.s};
+}
+__device__ __forceinline__ void rope_pair(float x0, float x1, Angle<F32T> a, float* y0, float* y1) {
+    rope_rot(x0, x1, a.c, a.s, y0, y1);
+}
+__device__ __forceinline__ void rope_pair(float x0, float x1, Angle<BF16T> a, float* y0, float* y1) {
+    *y0 = __fmaf_rn(x0, a.c, -(x1 * a.s));
+    *y1 = __fmaf_rn(x1, a.c, x0 * a.s);
+}
+
 template <class E> __device__ __forceinline__ void ld4(const char* p, float (&x)[4]);
 template <> __device__ __forceinline__ void ld4<F32T>(const char* p, float (&x)[4]) {
     const float4 v = gld<float4>(p);
@@ -157,7 +202,7 @@ template <> __device__ __forceinline__ void st4<BF16T, false>(char* p, const flo
 template <class E, int D, bool MOD>
 __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t) {
     constexpr int FR = 4, H2 = D / 2, CG = H2 / 4, VCH = D * E::E / 16;
-    __shared__ double cs[FR * H2 * 2];
+    __shared__ Angle<E> cs[FR * H2];
     const UnitMap& m = a.m;
     const int nfb = (m.n + FR - 1) / FR;
     const int unit = blockIdx.x / nfb, fb = blockIdx.x - unit * nfb;
@@ -167,10 +212,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
     const int f0 = fb * FR, nf = min(FR, m.n - f0);
     for (int x = threadIdx.x; x < nf * H2; x += blockDim.x) {
         const int f = x / H2, i = x - f * H2;
-        double c, s;
-        rope_angle(p0 + f0 + f, a.g.omega[i], &c, &s);
-        cs[2 * x] = c;
-        cs[2 * x + 1] = s;
+        cs[x] = rope_of<E>(p0 + f0 + f, a.g.omega[i]);
     }
     __syncthreads();
     const int hkv = a.g.hkv;
@@ -190,8 +232,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
         ld4<E>(src + (H2 + 4 * c) * E::E, x1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const double* an = cs + 2 * (f * H2 + 4 * c + q);
-            rope_rot(x0[q], x1[q], an[0], an[1], &y0[q], &y1[q]);
+            rope_pair(x0[q], x1[q], cs[f * H2 + 4 * c + q], &y0[q], &y1[q]);
         }
         char* dst = layer + (long long)h * a.g.slice_bytes + slot * (D * E::E);
         st4<E, true>(dst + 4 * c * E::E, y0);
@@ -364,7 +405,17 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
     char* Pw = Qs + L::QCAP + wave * L::PRB;
 
-    int b = blockIdx.x;
+    // Workgroup -> work item.  Workgroups go to the 8 XCDs round robin; each
+    // XCD is given a contiguous run of items (consecutive units, all head
+    // groups), so no XCD streams only one head group of every other unit.
+    // Measured on the 256-stream serving workload, the plain mapping left
+    // whole XCDs 15 % slower than others.
+    int b;
+    {
+        const int nb = gridDim.x, x = blockIdx.x & 7, s8 = blockIdx.x >> 3;
+        const int base = nb >> 3, rem = nb & 7;
+        b = x < rem ? x * (base + 1) + s8 : rem * (base + 1) + (x - rem) * base + s8;
+    }
     const int split = SPLIT ? b % a.n_splits : 0;
     if (SPLIT) b /= a.n_splits;
     const int qc = b % a.n_qchunks;
@@ -460,12 +511,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         const int j = r / group, gh = r - j * group;
         const int g = g0 + hh;
         const long long pos = pq0 + j;
-        double cs[4], sn[4];
+        Angle<E> an[4];
         float y0[4], y1[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rope_angle(pos, a.g.omega[4 * c + q], &cs[q], &sn[q]);
+        for (int q = 0; q < 4; ++q) an[q] = rope_of<E>(pos, a.g.omega[4 * c + q]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rope_rot(it.x0[q], it.x1[q], cs[q], sn[q], &y0[q], &y1[q]);
+        for (int q = 0; q < 4; ++q) rope_pair(it.x0[q], it.x1[q], an[q], &y0[q], &y1[q]);
         char* dst = Qs + (hh * R + r) * L::RB;
         st4<E, false>(dst + 4 * c * E::E, y0);
         st4<E, false>(dst + (H2 + 4 * c) * E::E, y1);
@@ -474,7 +525,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
             char* Vg = Kg + a.g.v_off;
             const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + j);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) rope_rot(it.k0[q], it.k1[q], cs[q], sn[q], &y0[q], &y1[q]);
+            for (int q = 0; q < 4; ++q) rope_pair(it.k0[q], it.k1[q], an[q], &y0[q], &y1[q]);
             char* kd = Kg + slot * L::RB;
             st4<E, true>(kd + 4 * c * E::E, y0);
             st4<E, true>(kd + (H2 + 4 * c) * E::E, y1);
@@ -723,23 +774,6 @@ static_assert(M4::QT == kQTileMfma, "query tile of the MFMA path");
 // A query's reference maximum moves only when a tile exceeds it by more than
 // this (log2 units), so unnormalised weights stay below 2^8.
 constexpr float kLazy = 8.0f;
-
-// (cos, sin) of a query rotation angle x = p * omega_i, 0 <= p < 2^31.  The
-// fp64 angle is reduced by 2 pi with a four-part Cody-Waite split whose first
-// three parts have 24 significant bits, so k * c_j is exact for |k| < 2^29
-// (every angle below 3.3e9 rad, which covers all positions the library
-// accepts) and the reduced angle is accurate to about 1e-15 rad; the
-// hardware sine / cosine then run on it in revolutions (1.2e-7 abs. error).
-struct CosSin { float c, s; };
-__device__ __forceinline__ CosSin rope_cs(double x) {
-    const double k = rint(x * 0x1.45f306dc9c883p-3);      // x / (2 pi)
-    x = fma(-k, 0x1.921fb60000000p+2, x);
-    x = fma(-k, -0x1.777a5c0000000p-23, x);
-    x = fma(-k, -0x1.ee59da0000000p-48, x);
-    x = fma(-k, 0x1.98a2e03707345p-75, x);
-    const float r = (float)(x * 0x1.45f306dc9c883p-3);
-    return CosSin{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
-}
 
 // max(a, b, c) in one instruction (operands are finite or the sentinel, so
 // no NaN handling is needed)
