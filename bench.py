@@ -10,12 +10,15 @@ c2 (default)  steady-state serving: 256 independent streams x 1 layer, 20
               step = one feed call that pushes 4 new frames into every stream:
               ring compaction where due, RoPE + append, windowed attention
               (one fused launch on the vector path).
+c1            64 streams x 32 layers, staggered ring phases, 4 frames per step
 c3            catch-up: 1 stream x 32 layers, bf16 N(0,1), 15300 frames fed as
               29 batches of 512 + one of 452 (the maximum batch), compactions
               before batches 4..30.  One step = one batch through all 32
               layers: compaction, RoPE + append, attention on the matrix
               cores.  The sequence restarts (host-only reset) after its last
               batch.
+c4            decoder step: 32 streams x 26 layers, GQA 32/8 x 128, window 8192.
+copy          calibration copy of 1 GiB for the HBM byte counters.
 
 All inputs of all timed steps are resident in HBM before the timed region.
 Prints one JSON line: frames/s over all streams (a frame counts once, after
@@ -87,6 +90,35 @@ def cpu_baseline(streams: int, layers_in_config: int, pre: int, steps: int, n: i
                       f"(rings pre-filled with {pre} frames, not timed), oracle.stream.EncStream "
                       f"in fp64 numpy on one thread, {elapsed:.1f} s for {frame_layers} "
                       f"frame-layers, divided by {layers_in_config} layer(s) per frame"}
+
+
+def cpu_baseline_dec(contexts, steps: int = 20):
+    """The fp64 oracle's decoder stream (oracle.stream.DecStream) on a bounded
+    sample: one layer of one stream at the median context, `steps` timed
+    single-token steps after an untimed fill; scaled to tokens/s through 26
+    layers."""
+    import numpy as np
+    from oracle import rope
+    from oracle.stream import DecStream
+    from synth import qkv
+
+    c = sorted(contexts)[len(contexts) // 2]
+    q, k, v = qkv(4, 0, 0, c + steps, 32, 8, 128, 1.0, "bf16")
+    st = DecStream(32, 8, 128)
+    # untimed fill of the oracle's ring (its own RoPE and ring model; no
+    # attention outputs are needed for the tokens before the timed steps)
+    kr = rope.apply(np.asarray(k[:c], dtype=np.float64), np.arange(c, dtype=np.int64), 1.0e6)
+    for p, slot in st.ring.append(c):
+        st.K[slot] = kr[p]
+        st.V[slot] = v[p]
+    t0 = time.perf_counter()
+    for j in range(steps):
+        st.step(q[c + j:c + j + 1], k[c + j:c + j + 1], v[c + j:c + j + 1])
+    el = time.perf_counter() - t0
+    return {"value": steps / el / 26, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one decoder layer of one stream at context {c} (the median), {steps} timed "
+                      f"single-token steps after an untimed ring fill, oracle.stream.DecStream in fp64 "
+                      f"numpy on one thread, {el:.1f} s; divided by 26 layers per token"}
 
 
 def _randn(gen, shape, scale, dev):
@@ -249,6 +281,103 @@ def bench_copy(args):
             "steps": args.steps}
 
 
+def bench_c1(args):
+    """64 streams x 32 independent layer caches, bf16 N(0,1)*0.5.  Stream i
+    first ingests o_i ~ U{0..749} frames (one untimed catch-up feed) so ring
+    phases and compactions are staggered, then pre-fills 750 more frames;
+    each timed step feeds 4 new frames to every stream, all 32 layers, in
+    one call."""
+    import torch
+    import sliding_window_cached_amd as vrt
+    from synth import offsets
+
+    dev = torch.device("cuda:0")
+    S, L, n = 64, 32, 4
+    off = [int(o) for o in offsets(1, S, 0, 750)]
+    desc = vrt.enc_desc(dtype=vrt.BF16, n_layers=L)
+    nb = vrt.state_device_bytes(desc)
+    mem = torch.empty(S * nb, dtype=torch.uint8, device=dev)
+    states = [vrt.StreamState(desc, mem[i * nb:(i + 1) * nb], nb, 0) for i in range(S)]
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    log("c1: staggered catch-up feeds and a 750-frame pre-fill per stream")
+    blk = [_randn(gen, (1, L, 750, H, D), 0.5, dev) for _ in range(3)]
+    ob = torch.empty_like(blk[0])
+    for i in range(S):
+        for m in ([off[i]] if off[i] else []) + [750]:
+            vrt.enc_attn_feed([states[i]], 0, L, *(x[:, :, :m].contiguous() for x in blk), m, ob, stream)
+    torch.cuda.synchronize()
+    del blk, ob
+    total = args.warmup + args.steps
+    log(f"c1: drawing inputs for {total} steps into HBM")
+    Q, K, V = (_randn(gen, (total, S, L, n, H, D), 0.5, dev) for _ in range(3))
+    out = torch.empty((S, L, n, H, D), dtype=torch.bfloat16, device=dev)
+    for i in range(args.warmup):
+        vrt.enc_attn_feed(states, 0, L, Q[i], K[i], V[i], n, out, stream)
+    torch.cuda.synchronize()
+    plan = []
+    nkv = [st.query(0)[1] for st in states]
+    for j in range(args.steps):
+        step = []
+        for i in range(S):
+            _, after, nc = vrt.ring_advance(desc, 0, nkv[i], n)
+            step.append((after - n, nc))
+            nkv[i] = after
+        plan.append(step)
+    ev = _timing_events(args.steps)
+    log(f"c1: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        i = args.warmup + j
+        vrt.set_attn_events(ev[j][0], ev[j][1])
+        vrt.enc_attn_feed(states, 0, L, Q[i], K[i], V[i], n, out, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    vrt.set_attn_events()
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    for st in states:
+        st.close()
+    nbytes = [L * sum(attn_work(k, n)[0] for k, _ in step) for step in plan]
+    t_attn = sum(attn_ms) * 1e-3
+    gbs = sum(nbytes) / t_attn / 1e9
+    return {
+        "metric": METRIC,
+        "value": S * n * args.steps / wall,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "64 streams x 32 layers, 20 heads x 64, window 750, ring 1536, bf16 N(0,1)*0.5, "
+                        "staggered ring phases (catch-up of U{0..749} frames, then 750), 4 frames per "
+                        "stream per step, all layers in one call",
+            "streams": S, "layers": L, "frames_per_step": n, "parallelism": "none (1 GPU)",
+            "compactions_timed": sum(nc for step in plan for _, nc in step),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_attn (vector path: fused RoPE + append + attention, 2048 units per launch)",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "alg_bytes_per_launch": nbytes[-1],
+            "launch_us_mean": t_attn / len(attn_ms) * 1e6,
+            "launches_timed": len(attn_ms),
+        },
+        "step_hbm_frac": sum(nbytes) / wall / 1e9 / HBM_PEAK_GBS,
+    }
+
+
 def c3_schedule(T=15300, B=512):
     return [min(B, T - t) for t in range(0, T, B)]
 
@@ -361,12 +490,133 @@ def bench_c3(args):
     }
 
 
+def bench_c4(args):
+    """Decoder step: 32 streams x 26 layers, GQA 32 query / 8 kv heads, head_dim
+    128, window 8192, modulo ring, bf16 N(0,1).  Contexts: 24 streams
+    uniform in [39, 8192], 8 streams uniform in [8193, 10269] (past the ring
+    wrap).  Each cache is filled through the library (untimed): a 39-token
+    prefill, prefills of up to 512 tokens up to the wrap, then single-token
+    steps; the filled keys are random (one 512-token block of inputs reused).
+    One step = one token for every stream through all 26 layers (split-K
+    attention over the window, then the merge)."""
+    import torch
+    import sliding_window_cached_amd as vrt
+    from synth import offsets
+
+    dev = torch.device("cuda:0")
+    S, L, HQ, HK, DD, WIN = 32, 26, 32, 8, 128, 8192
+    ctx = [int(c) for c in offsets(4, 24, 39, 8193)] + [int(c) for c in offsets(4, 8, 8193, 10270)]
+    desc = vrt.dec_desc(dtype=vrt.BF16, n_layers=L)
+    nb = vrt.state_device_bytes(desc)
+    mem = torch.empty(S * nb, dtype=torch.uint8, device=dev)
+    states = [vrt.StreamState(desc, mem[i * nb:(i + 1) * nb], nb, 0) for i in range(S)]
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    B = 512
+    qb = _randn(gen, (1, L, B, HQ, DD), 1.0, dev)
+    kb = _randn(gen, (1, L, B, HK, DD), 1.0, dev)
+    vb = _randn(gen, (1, L, B, HK, DD), 1.0, dev)
+    ob = torch.empty_like(qb)
+    ws1 = vrt.dec_workspace_bytes(desc, 1, L, 1)
+    wsb = vrt.dec_workspace_bytes(desc, S, L, 1)
+    ws = torch.empty(max(ws1, wsb) // 4 + 1, dtype=torch.float32, device=dev)
+    log(f"c4: filling 32 decoder caches (26 layers) to contexts {min(ctx)}..{max(ctx)}")
+    t_fill = time.perf_counter()
+    for i in range(S):
+        n = 0
+        for m in [39] + [B] * 64:
+            m = min(m, min(ctx[i], WIN) - n)
+            if m <= 0:
+                break
+            def sl(x, m=m):
+                return x[:, :, :m].contiguous()
+            vrt.dec_attn_step([states[i]], 0, L, sl(qb), sl(kb), sl(vb), m, ob, stream=stream)
+            n += m
+    # single-token steps past the wrap, all long streams together
+    q1, k1, v1, o1 = (x[:, :, :1].expand(S, L, 1, x.shape[3], DD).contiguous()
+                      for x in (qb, kb, vb, ob))
+    while True:
+        need = [i for i in range(S) if states[i].query(0)[1] < ctx[i]]
+        if not need:
+            break
+        k = len(need)
+        vrt.dec_attn_step([states[i] for i in need], 0, L, q1[:k], k1[:k], v1[:k], 1, o1[:k], ws,
+                          wsb, stream)
+    torch.cuda.synchronize()
+    log(f"c4: filled in {time.perf_counter() - t_fill:.1f} s")
+    total = args.warmup + args.steps
+    Q = _randn(gen, (total, S, L, 1, HQ, DD), 1.0, dev)
+    K = _randn(gen, (total, S, L, 1, HK, DD), 1.0, dev)
+    V = _randn(gen, (total, S, L, 1, HK, DD), 1.0, dev)
+    out = torch.empty((S, L, 1, HQ, DD), dtype=torch.bfloat16, device=dev)
+    for j in range(args.warmup):
+        vrt.dec_attn_step(states, 0, L, Q[j], K[j], V[j], 1, out, ws, wsb, stream)
+    torch.cuda.synchronize()
+    seen = []   # keys each unit's step attends to
+    for j in range(args.steps):
+        seen.append([min(WIN, states[i].query(0)[1] + j + 1) for i in range(S)])
+    ev = _timing_events(args.steps)
+    log(f"c4: timing {args.steps} decode steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        i = args.warmup + j
+        vrt.set_attn_events(ev[j][0], ev[j][1])
+        vrt.dec_attn_step(states, 0, L, Q[i], K[i], V[i], 1, out, ws, wsb, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    vrt.set_attn_events()
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    for st in states:
+        st.close()
+    # algorithmic bytes of one step: every unit reads the K and V rows of its
+    # window (8 kv heads x 128 x bf16) and its q; writes its new K/V row and out
+    row = HK * DD * 2
+    nbytes = [L * sum(2 * n * row + (2 * HQ * DD * 2) + 2 * row for n in w) for w in seen]
+    t_attn = sum(attn_ms) * 1e-3
+    gbs = sum(nbytes) / t_attn / 1e9
+    return {
+        "metric": "decoder tokens/s through the cached window-8192 GQA step (all streams, 26 layers each)",
+        "value": S * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decoder step: 32 streams x 26 layers, GQA 32/8 heads x 128, window 8192, "
+                        "modulo ring 8192, bf16 N(0,1); contexts 24 x U[39, 8192] and 8 x "
+                        "U[8193, 10269]; one step = one token per stream",
+            "streams": S, "layers": L, "heads_q": HQ, "heads_kv": HK, "head_dim": DD, "window": WIN,
+            "contexts": ctx, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_attn split-K (kv heads x 1024-key splits) + k_dec_combine",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "alg_bytes_per_launch": nbytes[-1],
+            "launch_us_mean": t_attn / len(attn_ms) * 1e6,
+            "launches_timed": len(attn_ms),
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "copy"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -383,10 +633,18 @@ def main():
         args.steps = 1000 if args.steps is None else args.steps
         args.warmup = 20 if args.warmup is None else args.warmup
         res = bench_c2(args)
-    else:
+    elif args.config == "c1":
+        args.steps = 200 if args.steps is None else args.steps
+        args.warmup = 10 if args.warmup is None else args.warmup
+        res = bench_c1(args)
+    elif args.config == "c3":
         args.steps = 300 if args.steps is None else args.steps
         args.warmup = 30 if args.warmup is None else args.warmup
         res = bench_c3(args)
+    else:
+        args.steps = 100 if args.steps is None else args.steps
+        args.warmup = 5 if args.warmup is None else args.warmup
+        res = bench_c4(args)
     if args.no_cpu_baseline:
         res["cpu_baseline"] = None
     else:
@@ -395,8 +653,12 @@ def main():
         if args.config == "c2":
             res["cpu_baseline"] = cpu_baseline(1, 1, W, 400, 4, 0.5, offsets(2, 1, 10 ** 4, 10 ** 6),
                                                "steady-state sample")
-        else:
+        elif args.config == "c1":
+            res["cpu_baseline"] = cpu_baseline(1, 32, W, 400, 4, 0.5, [0], "staggered-streams sample")
+        elif args.config == "c3":
             res["cpu_baseline"] = cpu_baseline(1, 32, 0, 4, 512, 1.0, [0], "catch-up sample")
+        else:
+            res["cpu_baseline"] = cpu_baseline_dec(res["config"]["contexts"])
     print(json.dumps(res), flush=True)
 
 
