@@ -405,13 +405,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
     char* Pw = Qs + L::QCAP + wave * L::PRB;
 
-    // Workgroup -> work item.  Workgroups go to the 8 XCDs round robin; each
-    // XCD is given a contiguous run of items (consecutive units, all head
-    // groups), so no XCD streams only one head group of every other unit.
-    // Measured on the 256-stream serving workload, the plain mapping left
-    // whole XCDs 15 % slower than others.
-    int b;
-    {
+    // Workgroup -> work item.  Workgroups go to the 8 XCDs round robin.
+    // Without splits each XCD is given a contiguous run of items (consecutive
+    // units, all head groups), so no XCD streams only one head group of every
+    // other unit: measured on the 256-stream serving workload, the plain
+    // mapping left whole XCDs 15 % slower than others.  With splits the work
+    // per unit follows its context length, so contiguous runs would hand the
+    // long units to a few XCDs; there the plain order deals the splits of
+    // every unit across all XCDs instead.
+    int b = blockIdx.x;
+    if (!SPLIT) {
         const int nb = gridDim.x, x = blockIdx.x & 7, s8 = blockIdx.x >> 3;
         const int base = nb >> 3, rem = nb & 7;
         b = x < rem ? x * (base + 1) + s8 : rem * (base + 1) + (x - rem) * base + s8;
@@ -455,7 +458,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         const char* Kg = layer + (long long)(g0 + hh) * a.g.slice_bytes;
         const char* Vg = Kg + a.g.v_off;
         const long long TB = (tfirst + it) * kTile;
-        const long long sb = MOD ? (TB % a.g.slots) : (TB - avail);
+        // 0 <= TB < 2^31 (positions are below 2^31), so 32-bit arithmetic is exact
+        const long long sb = MOD ? (long long)((unsigned)TB % (unsigned)a.g.slots) : (TB - avail);
         const int rlo = (int)max(0LL, wlo - TB), rhi = (int)min(63LL, whi - TB);
         char* ks = lds + st * 2 * L::TILE;
         char* vs = ks + L::TILE;
