@@ -20,6 +20,10 @@ c3            catch-up: 1 stream x 32 layers, bf16 N(0,1), 15300 frames fed as
 c4            decoder step: 32 streams x 26 layers, GQA 32/8 x 128, window 8192.
 copy          calibration copy of 1 GiB for the HBM byte counters.
 
+--ring mod runs c1, c2 or c3 with the encoder cache kept as a modulo ring
+(1280 slots, slot = position % slots, no compaction; outputs bit-identical
+to the compacting ring).
+
 All inputs of all timed steps are resident in HBM before the timed region.
 Prints one JSON line: frames/s over all streams (a frame counts once, after
 every layer of the configuration has processed it), the roofline of the
@@ -41,7 +45,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
-H, D, W, SLOTS = 20, 64, 750, 1536
+H, D, W = 20, 64, 750
 R = H * D
 METRIC = "encoder frames/s through cached window-750 attention (all streams); % HBM peak"
 
@@ -127,6 +131,18 @@ def _randn(gen, shape, scale, dev):
     return (x * scale).to(torch.bfloat16)
 
 
+def enc_desc(args, layers):
+    import sliding_window_cached_amd as vrt
+    kind = vrt.ENC_MODRING if args.ring == "mod" else vrt.ENC_RING
+    return vrt.enc_desc(dtype=vrt.BF16, n_layers=layers, kind=kind)
+
+
+def ring_words(desc) -> str:
+    if desc.kind == 0:
+        return f"{desc.ring_slots}-slot ring compacted to its last 750 frames when full"
+    return f"{desc.ring_slots}-slot modulo ring (slot = position % {desc.ring_slots}, no compaction)"
+
+
 def _timing_events(n):
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -145,7 +161,7 @@ def bench_c2(args):
 
     dev = torch.device("cuda:0")
     S, n = 256, 4
-    desc = vrt.enc_desc(dtype=vrt.BF16, n_layers=1)
+    desc = enc_desc(args, 1)
     starts = offsets(2, S, 10 ** 4, 10 ** 6)
     nb = vrt.state_device_bytes(desc)
     mem = torch.empty(S * nb, dtype=torch.uint8, device=dev)
@@ -218,10 +234,11 @@ def bench_c2(args):
         "data": "synthetic",
         "config": {
             "workload": "steady-state serving: 256 streams x 1 layer, 20 heads x 64, window 750, "
-                        "1536-slot ring pre-filled to 750, 4 frames per stream per step, bf16 "
+                        f"{ring_words(desc)} pre-filled to 750, 4 frames per stream per step, bf16 "
                         "N(0,1)*0.5, start positions U[1e4, 1e6)",
             "streams": S, "layers": 1, "frames_per_step": n, "heads": H, "head_dim": D,
-            "window": W, "ring_slots": SLOTS, "parallelism": "none (1 GPU)",
+            "window": W, "ring_slots": desc.ring_slots, "ring": args.ring,
+            "parallelism": "none (1 GPU)",
         },
         "roofline": {
             "bound": "hbm",
@@ -299,7 +316,7 @@ def bench_c1(args):
     dev = torch.device("cuda:0")
     S, L, n = 64, 32, 4
     off = [int(o) for o in offsets(1, S, 0, 750)]
-    desc = vrt.enc_desc(dtype=vrt.BF16, n_layers=L)
+    desc = enc_desc(args, L)
     nb = vrt.state_device_bytes(desc)
     mem = torch.empty(S * nb, dtype=torch.uint8, device=dev)
     states = [vrt.StreamState(desc, mem[i * nb:(i + 1) * nb], nb, 0) for i in range(S)]
@@ -361,10 +378,11 @@ def bench_c1(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "64 streams x 32 layers, 20 heads x 64, window 750, ring 1536, bf16 N(0,1)*0.5, "
+            "workload": f"64 streams x 32 layers, 20 heads x 64, window 750, {ring_words(desc)}, bf16 N(0,1)*0.5, "
                         "staggered ring phases (catch-up of U{0..749} frames, then 750), 4 frames per "
                         "stream per step, all layers in one call",
-            "streams": S, "layers": L, "frames_per_step": n, "parallelism": "none (1 GPU)",
+            "streams": S, "layers": L, "frames_per_step": n, "ring_slots": desc.ring_slots,
+            "ring": args.ring, "parallelism": "none (1 GPU)",
             "compactions_timed": sum(nc for step in plan for _, nc in step),
         },
         "roofline": {
@@ -394,7 +412,7 @@ def bench_c3(args):
     dev = torch.device("cuda:0")
     L, start = 32, 0
     sched = c3_schedule()
-    desc = vrt.enc_desc(dtype=vrt.BF16, n_layers=L)
+    desc = enc_desc(args, L)
     nb = vrt.state_device_bytes(desc)
     mem = torch.empty(nb, dtype=torch.uint8, device=dev)
     st = vrt.StreamState(desc, mem, nb, start)
@@ -468,11 +486,12 @@ def bench_c3(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "catch-up: 1 stream x 32 layers, 20 heads x 64, window 750, ring 1536, "
-                        "15300 frames as 29 x 512 + 452 (max batch 512), compactions between "
-                        "batches, bf16 N(0,1); one step = one batch through all 32 layers",
+            "workload": f"catch-up: 1 stream x 32 layers, 20 heads x 64, window 750, {ring_words(desc)}, "
+                        "15300 frames as 29 x 512 + 452 (max batch 512), bf16 N(0,1); one step = "
+                        "one batch through all 32 layers",
             "streams": 1, "layers": L, "frames": sum(sched), "max_batch": 512, "heads": H,
-            "head_dim": D, "window": W, "ring_slots": SLOTS, "parallelism": "none (1 GPU)",
+            "head_dim": D, "window": W, "ring_slots": desc.ring_slots, "ring": args.ring,
+            "parallelism": "none (1 GPU)",
         },
         "roofline": {
             "bound": "mfma",
@@ -623,6 +642,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring", default="compact", choices=["compact", "mod"],
+                    help="encoder configs: compacting ring (the pages') or modulo ring")
     ap.add_argument("--timing-every", type=int, default=10,
                     help="c2: record the attention-kernel events on every N-th timed step")
     args = ap.parse_args()

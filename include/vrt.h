@@ -67,7 +67,8 @@ typedef enum { VRT_F32 = 0, VRT_BF16 = 1 } vrt_dtype;
 
 typedef enum {
     VRT_ENC_RING = 0,     /* encoder: contiguous ring + compaction */
-    VRT_DEC_MODRING = 1   /* decoder: slot = position % ring_slots */
+    VRT_DEC_MODRING = 1,  /* decoder: slot = position % ring_slots */
+    VRT_ENC_MODRING = 2   /* encoder: slot = position % ring_slots, no compaction */
 } vrt_cache_kind;
 
 /* Everything about a cache is fixed when its states are created
@@ -75,7 +76,15 @@ typedef enum {
  * Encoder on the pages: kind ENC_RING, 20 heads (q = kv), head_dim 64,
  * window 750, ring_slots 1536, max_batch 512, rope_theta 1e6, 32 layers.
  * Decoder: kind DEC_MODRING, 32 q / 8 kv heads, head_dim 128,
- * window = ring_slots = 8192, rope_theta 1e6, 26 layers. */
+ * window = ring_slots = 8192, rope_theta 1e6, 26 layers.
+ * ENC_MODRING is the encoder cache stored the decoder's way (family doc,
+ * Streaming row item 5: slot = position % ring_slots, positions stay
+ * absolute): the same feeds, masks and arithmetic as ENC_RING without the
+ * compaction copies, so its outputs are bit-identical to ENC_RING's (the
+ * pages validate their decoder ring the same way, by an A/B against a buffer
+ * that never wraps).  It needs ring_slots >= window - 1 + max_batch (a
+ * sub-batch never overwrites a row one of its own queries reads), a multiple
+ * of 64 (a 64-key tile never wraps); 1280 for the encoder above. */
 typedef struct {
     int32_t kind;        /* vrt_cache_kind */
     int32_t dtype;       /* vrt_dtype: storage and I/O type; accumulation is fp32 */
@@ -84,8 +93,10 @@ typedef struct {
     int32_t n_heads_kv;  /* key/value heads */
     int32_t head_dim;    /* 64 or 128 */
     int32_t window;      /* W: a query at p sees keys in (p - W, p] */
-    int32_t ring_slots;  /* ENC: >= window + max_batch; DEC: >= window, multiple of 64 */
-    int32_t max_batch;   /* ENC: largest sub-batch per append (feeds are split) */
+    int32_t ring_slots;  /* ENC_RING: >= window + max_batch; DEC_MODRING: >= window,
+                            multiple of 64; ENC_MODRING: >= window - 1 + max_batch,
+                            multiple of 64 */
+    int32_t max_batch;   /* encoder kinds: largest sub-batch per append (feeds are split) */
     int32_t reserved;    /* must be 0 */
     double rope_theta;   /* NEOX RoPE base; omega_i = theta^(-2i/head_dim) */
 } vrt_cache_desc;
@@ -104,10 +115,12 @@ const char* vrt_last_device_error(void);
 
 /* Check a descriptor without creating anything.  VRT_ERR_INVALID for
  * non-positive sizes or a reserved field != 0; VRT_ERR_UNSUPPORTED for a
- * head_dim other than 64/128, an unknown dtype/kind, an encoder ring smaller
+ * head_dim other than 64/128, an unknown dtype/kind, an ENC_RING ring smaller
  * than window + max_batch (streaming-plan page, "Unbounded length": batches
  * of at most 512 frames so one feed can never overflow the 1536-slot ring),
- * or a decoder ring smaller than the window or not a multiple of 64. */
+ * a decoder ring smaller than the window or not a multiple of 64, or an
+ * ENC_MODRING ring smaller than window - 1 + max_batch or not a multiple
+ * of 64. */
 vrt_status vrt_desc_check(const vrt_cache_desc* desc);
 
 /* Device bytes one state needs: for each layer a K ring and a V ring, each
@@ -138,8 +151,9 @@ void vrt_stream_state_destroy(vrt_stream_state* st);
 
 /* Host mirror of one layer's ring: abs_base = absolute position held in slot
  * 0 (streaming-plan page, "Unbounded length": stream_enc_abs_base), n_kv =
- * rows held.  For a decoder state abs_base is the stream's first position and
- * n_kv counts every token written (slot of position p is p % ring_slots). */
+ * rows held.  For a modulo-ring state (DEC_MODRING, ENC_MODRING) abs_base is
+ * the stream's first position and n_kv counts every token written (slot of
+ * position p is p % ring_slots). */
 vrt_status vrt_stream_state_query(const vrt_stream_state* st, int layer, int64_t* abs_base,
                                   int32_t* n_kv);
 
@@ -148,14 +162,17 @@ vrt_status vrt_stream_state_query(const vrt_stream_state* st, int layer, int64_t
  * length": contiguous writes, compaction keeping the last `window` frames
  * when the ring would overflow, feeds split into <= max_batch sub-batches).
  * Applies a feed of n_new frames to (*abs_base, *n_kv) in place and returns
- * in *n_compactions how many compactions it implies.  No device work. */
+ * in *n_compactions how many compactions it implies.  For ENC_MODRING it
+ * only adds n_new to *n_kv (no compaction).  No device work.
+ * VRT_ERR_INVALID for a decoder desc. */
 vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32_t* n_kv,
                             int n_new, int32_t* n_compactions);
 
 /* Which attention path a sub-batch of n frames takes: 0 = vector-ALU kernel
  * (fp32 dot products), 1 = matrix-core kernel (bf16 MFMA products, fp32
  * accumulation).  A pure function of the desc and n: 1 exactly for encoder
- * descs with bf16 storage, head_dim 64, n_heads_q == n_heads_kv and n >= 32;
+ * descs (either kind) with bf16 storage, head_dim 64, n_heads_q == n_heads_kv
+ * and n >= 32;
  * 0 otherwise; -1 for an invalid desc or n < 1.  A feed is split into
  * sub-batches of at most max_batch frames and each takes its own path; the
  * offline call is one sub-batch of T frames.  Outputs are bit-identical
@@ -181,9 +198,9 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
  * n_states encoder states (streaming-plan page, "Mechanism": the chunk's K/V
  * are written at rows [n_kv_before, n_kv_total) and the queries then read
  * rows [0, n_kv_total) under the windowed mask).  Per (state, layer) and per
- * sub-batch of <= max_batch frames: compaction if needed, RoPE + append,
- * then attention of the sub-batch's queries (each new query also sees the
- * earlier new frames of its feed).
+ * sub-batch of <= max_batch frames: compaction if needed (ENC_RING only),
+ * RoPE + append, then attention of the sub-batch's queries (each new query
+ * also sees the earlier new frames of its feed).
  * q/out: [n_states][n_layers][n_new][n_heads_q][head_dim];
  * k/v:   [n_states][n_layers][n_new][n_heads_kv][head_dim].
  * All states must share one desc (field-wise equal) and be distinct.
@@ -196,7 +213,8 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* states, int n_states, int 
 /* Compact layers [layer0, layer0 + n_layers) of each state now: keep the last
  * `window` rows at the front (streaming-plan page, "Unbounded length": copy
  * the last 750 frames to the front).  A no-op for a layer with
- * n_kv <= window.  Encoder states only. */
+ * n_kv <= window, and for ENC_MODRING states (nothing is ever compacted).
+ * Encoder states only. */
 vrt_status vrt_ring_compact(vrt_stream_state* const* states, int n_states, int layer0,
                             int n_layers, hipStream_t stream);
 

@@ -18,7 +18,9 @@ Readings where the pages leave a step open:
 
 Decoder ring (family doc, Streaming row item 5): token ``cur`` goes to slot
 ``cur % n_ctx``; positions stay absolute; with n_ctx = window = 8192 the slot
-being overwritten holds cur - 8192, one past the window.
+being overwritten holds cur - 8192, one past the window.  The same model
+describes the encoder cache kept as a modulo ring instead of a compacting
+one (every position p lives in slot p % slots).
 """
 from __future__ import annotations
 

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvrt.so")
 
 F32, BF16 = 0, 1
-ENC_RING, DEC_MODRING = 0, 1
+ENC_RING, DEC_MODRING, ENC_MODRING = 0, 1, 2
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE, ERR_POISONED = range(6)
 
 EXPORTS = (
@@ -41,10 +41,15 @@ class CacheDesc(Structure):
     ]
 
 
-def enc_desc(dtype=BF16, n_layers=1, heads=20, head_dim=64, window=750, ring_slots=1536,
-             max_batch=512, theta=1.0e6) -> CacheDesc:
-    """Encoder cache as on the pages: 20 heads x 64, window 750, 1536 slots."""
-    return CacheDesc(ENC_RING, dtype, n_layers, heads, heads, head_dim, window, ring_slots,
+def enc_desc(dtype=BF16, n_layers=1, heads=20, head_dim=64, window=750, ring_slots=None,
+             max_batch=512, theta=1.0e6, kind=ENC_RING) -> CacheDesc:
+    """Encoder cache as on the pages: 20 heads x 64, window 750, 1536 slots
+    (kind ENC_RING, compaction).  kind=ENC_MODRING stores the same cache as a
+    modulo ring (slot = position % ring_slots, no compaction); its default
+    ring is window - 1 + max_batch rounded up to a multiple of 64 (1280)."""
+    if ring_slots is None:
+        ring_slots = 1536 if kind == ENC_RING else -(-(window - 1 + max_batch) // 64) * 64
+    return CacheDesc(kind, dtype, n_layers, heads, heads, head_dim, window, ring_slots,
                      max_batch, 0, theta)
 
 

@@ -71,7 +71,8 @@ bool same_desc(const vrt_cache_desc& a, const vrt_cache_desc& b) {
 vrt_status check_desc(const vrt_cache_desc* d) {
     if (!d) return VRT_ERR_INVALID;
     if (d->reserved != 0) return VRT_ERR_INVALID;
-    if (d->kind != VRT_ENC_RING && d->kind != VRT_DEC_MODRING) return VRT_ERR_UNSUPPORTED;
+    if (d->kind != VRT_ENC_RING && d->kind != VRT_DEC_MODRING && d->kind != VRT_ENC_MODRING)
+        return VRT_ERR_UNSUPPORTED;
     if (d->dtype != VRT_F32 && d->dtype != VRT_BF16) return VRT_ERR_UNSUPPORTED;
     if (d->n_layers < 1 || d->n_heads_q < 1 || d->n_heads_kv < 1 || d->window < 1 ||
         d->ring_slots < 1 || d->max_batch < 1)
@@ -85,10 +86,20 @@ vrt_status check_desc(const vrt_cache_desc* d) {
         return VRT_ERR_UNSUPPORTED;
     if (d->kind == VRT_ENC_RING) {
         if ((int64_t)d->ring_slots < (int64_t)d->window + d->max_batch) return VRT_ERR_UNSUPPORTED;
+    } else if (d->kind == VRT_ENC_MODRING) {
+        // a sub-batch of max_batch frames, written before its attention, must
+        // not overwrite the oldest key (window - 1 back) its first query reads
+        if ((int64_t)d->ring_slots < (int64_t)d->window - 1 + d->max_batch ||
+            d->ring_slots % kTile != 0)
+            return VRT_ERR_UNSUPPORTED;
     } else {
         if (d->ring_slots < d->window || d->ring_slots % kTile != 0) return VRT_ERR_UNSUPPORTED;
     }
     return VRT_OK;
+}
+
+bool is_encoder(const vrt_cache_desc& d) {
+    return d.kind == VRT_ENC_RING || d.kind == VRT_ENC_MODRING;
 }
 
 size_t slice_bytes(const vrt_cache_desc& d) {
@@ -105,7 +116,7 @@ Geom make_geom(const vrt_cache_desc& d) {
     g.group = d.n_heads_q / d.n_heads_kv;
     g.slots = d.ring_slots;
     g.window = d.window;
-    g.mod = d.kind == VRT_DEC_MODRING ? 1 : 0;
+    g.mod = d.kind == VRT_ENC_RING ? 0 : 1;
     g.slice_bytes = (long long)slice_bytes(d);
     g.v_off = (long long)d.n_heads_kv * g.slice_bytes;
     g.layer_bytes = 2 * g.v_off;
@@ -143,7 +154,7 @@ int pick_hg(const Geom& g, long long units, int rows_per_head, long long qchunks
 // description and n, so two feeds that split a sequence differently but take
 // the same path produce bit-identical outputs.
 bool use_mfma(const vrt_cache_desc& d, int n) {
-    return d.kind == VRT_ENC_RING && d.dtype == VRT_BF16 && d.head_dim == 64 &&
+    return is_encoder(d) && d.dtype == VRT_BF16 && d.head_dim == 64 &&
            d.n_heads_q == d.n_heads_kv && n >= kMfmaMinFrames;
 }
 
@@ -379,7 +390,14 @@ vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32
                             int n_new, int32_t* n_compactions) {
     const vrt_status s = check_desc(desc);
     if (s != VRT_OK) return s;
-    if (desc->kind != VRT_ENC_RING || !abs_base || !n_kv || n_new < 0) return VRT_ERR_INVALID;
+    if (!is_encoder(*desc) || !abs_base || !n_kv || n_new < 0) return VRT_ERR_INVALID;
+    if (desc->kind == VRT_ENC_MODRING) {   // every frame is kept: n_kv counts them all
+        if (*n_kv < 0 || *abs_base < 0 || *abs_base + *n_kv > kPosLimit - n_new)
+            return VRT_ERR_INVALID;
+        *n_kv += n_new;
+        if (n_compactions) *n_compactions = 0;
+        return VRT_OK;
+    }
     if (*n_kv < 0 || *n_kv > desc->ring_slots) return VRT_ERR_INVALID;
     int64_t base = *abs_base;
     int32_t nkv = *n_kv, nc = 0;
@@ -412,7 +430,7 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
                                 void* scratch, size_t scratch_bytes, hipStream_t stream) {
     const vrt_status s = check_desc(desc);
     if (s != VRT_OK) return s;
-    if (desc->kind != VRT_ENC_RING) return VRT_ERR_INVALID;
+    if (!is_encoder(*desc)) return VRT_ERR_INVALID;
     if (!q || !k || !v || !out || !scratch || T < 1) return VRT_ERR_INVALID;
     if (start_pos < 0 || start_pos > kPosLimit - T) return VRT_ERR_INVALID;
     if (scratch_bytes < vrt_offline_scratch_bytes(desc, T)) return VRT_ERR_CAPACITY;
@@ -460,7 +478,8 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
 vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int layer0,
                              int n_layers, const void* q, const void* k, const void* v,
                              int n_new, void* out, hipStream_t stream) {
-    vrt_status s = check_batch(st, n_states, layer0, n_layers, VRT_ENC_RING);
+    if (!st || n_states < 1 || !st[0] || !is_encoder(st[0]->d)) return VRT_ERR_INVALID;
+    vrt_status s = check_batch(st, n_states, layer0, n_layers, st[0]->d.kind);
     if (s != VRT_OK) return s;
     if (!q || !k || !v || !out || n_new < 1) return VRT_ERR_INVALID;
     for (int i = 0; i < n_states; ++i)
@@ -473,9 +492,10 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
     int t0 = 0;
     for (int m : split_feed(n_new, d.max_batch)) {
         std::vector<std::pair<int, int>> comp;
-        for (int i = 0; i < n_states; ++i)
-            for (int l = layer0; l < layer0 + n_layers; ++l)
-                if (st[i]->n_kv[l] + m > d.ring_slots) comp.emplace_back(i, l);
+        if (d.kind == VRT_ENC_RING)
+            for (int i = 0; i < n_states; ++i)
+                for (int l = layer0; l < layer0 + n_layers; ++l)
+                    if (st[i]->n_kv[l] + m > d.ring_slots) comp.emplace_back(i, l);
         if (run_compactions(st, comp, stream) != hipSuccess) {
             poison(st, n_states);
             return VRT_ERR_DEVICE;
@@ -513,8 +533,10 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
 
 vrt_status vrt_ring_compact(vrt_stream_state* const* st, int n_states, int layer0, int n_layers,
                             hipStream_t stream) {
-    const vrt_status s = check_batch(st, n_states, layer0, n_layers, VRT_ENC_RING);
+    if (!st || n_states < 1 || !st[0] || !is_encoder(st[0]->d)) return VRT_ERR_INVALID;
+    const vrt_status s = check_batch(st, n_states, layer0, n_layers, st[0]->d.kind);
     if (s != VRT_OK) return s;
+    if (st[0]->d.kind == VRT_ENC_MODRING) return VRT_OK;   // a modulo ring is never compacted
     std::vector<std::pair<int, int>> comp;
     for (int i = 0; i < n_states; ++i)
         for (int l = layer0; l < layer0 + n_layers; ++l)

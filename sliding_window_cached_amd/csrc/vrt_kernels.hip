@@ -835,7 +835,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
 
     auto issue = [&](int T, int st) {
         const long long TB = T0 + (long long)T * kTile;
-        const long long sb = TB - avail;
+        // modulo ring: 0 <= TB < 2^31 and the slot count is a multiple of 64,
+        // so a tile is contiguous in the ring and 32-bit arithmetic is exact
+        const long long sb = a.g.mod ? (long long)((unsigned)TB % (unsigned)a.g.slots) : TB - avail;
         const int rlo = (int)max(0LL, wlo - TB), rhi = (int)min(63LL, whi - TB);
         char* ks = lds + st * 2 * L::TILE;
         char* vs = ks + L::TILE;
@@ -1194,7 +1196,7 @@ hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t 
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t s) {
-    if (a.g.dtype != 1 || a.g.D != 64 || a.g.group != 1 || a.g.mod || a.n_splits != 1)
+    if (a.g.dtype != 1 || a.g.D != 64 || a.g.group != 1 || a.n_splits != 1)
         return hipErrorInvalidValue;
     const long long blocks = (long long)a.m.n_states * a.m.nl * a.g.hkv * a.n_qchunks;
     hipLaunchKernelGGL(k_attn_mfma, dim3((unsigned)blocks), dim3(256), 0, s, a, t);

@@ -10,7 +10,7 @@ import re
 import pytest
 
 import sliding_window_cached_amd as vrt
-from oracle.ring import EncRing
+from oracle.ring import DecRing, EncRing
 
 HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vrt.h")
 
@@ -202,3 +202,46 @@ def test_single_hip_runtime_in_process():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root)
     assert r.returncode == 0, r.stderr
     assert r.stdout.split("\n")[0] == "1", r.stdout
+
+
+def test_modulo_encoder_ring_host_rules():
+    """ENC_MODRING (the encoder cache as a modulo ring): ring_slots must hold
+    window - 1 + max_batch rows and be a multiple of 64; the planner never
+    compacts and counts every frame, as the oracle's modulo-ring model does;
+    the attention path is the same function of n as for the compacting ring;
+    an explicit compaction is a no-op; modulo and compacting states never mix
+    in one call."""
+    M = vrt.ENC_MODRING
+    d = vrt.enc_desc(kind=M)
+    assert d.ring_slots == 1280 and vrt.desc_check(d) == vrt.OK
+    assert vrt.desc_check(vrt.enc_desc(kind=M, ring_slots=1216)) == vrt.ERR_UNSUPPORTED  # < 1261
+    assert vrt.desc_check(vrt.enc_desc(kind=M, ring_slots=1261)) == vrt.ERR_UNSUPPORTED  # not 64k
+    assert vrt.desc_check(vrt.enc_desc(kind=M, ring_slots=1536)) == vrt.OK
+    assert vrt.desc_check(vrt.enc_desc(kind=M, window=256, max_batch=64)) == vrt.OK   # 320 slots
+    assert vrt.enc_desc(kind=M, window=256, max_batch=64).ring_slots == 320
+    assert vrt.state_device_bytes(vrt.enc_desc(kind=M, n_layers=32)) == 32 * 2 * 20 * 1280 * 64 * 2
+    rng = random.Random(1)
+    for _ in range(50):
+        r = DecRing(slots=1280)
+        start = rng.randrange(0, 10 ** 6)
+        r.reset(start)
+        base, nkv = start, 0
+        for _ in range(rng.randrange(1, 30)):
+            n = rng.choice([1, 4, 31, 32, 512, 513, 2000])
+            r.append(n)
+            base, nkv, nc = vrt.ring_advance(d, base, nkv, n)
+            assert nc == 0 and base == start and base + nkv == r.next_pos
+    for n in (1, 4, 31, 32, 512):
+        assert vrt.attn_path(d, n) == vrt.attn_path(vrt.enc_desc(), n)
+    assert vrt.attn_path(vrt.enc_desc(kind=M, dtype=vrt.F32), 512) == 0
+    st = _state(vrt.enc_desc(kind=M, n_layers=2), 5)
+    vrt.ring_compact([st], 0, 2)                      # nothing to compact, nothing enqueued
+    assert st.query(1) == (5, 0)
+    ring = _state(vrt.enc_desc(n_layers=2))
+    P = FAKE
+    assert vrt.enc_attn_feed([st, ring], 0, 1, P, P, P, 4, P, 0, check=False) == vrt.ERR_INVALID
+    lim = 2 ** 31
+    top = _state(vrt.enc_desc(kind=M), lim - 3)
+    assert vrt.enc_attn_feed([top], 0, 1, P, P, P, 4, P, 0, check=False) == vrt.ERR_INVALID
+    with pytest.raises(vrt.VrtError):
+        vrt.ring_advance(vrt.enc_desc(kind=M), lim - 3, 0, 4)
