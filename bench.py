@@ -234,7 +234,7 @@ def bench_c2(args):
         "data": "synthetic",
         "config": {
             "workload": "steady-state serving: 256 streams x 1 layer, 20 heads x 64, window 750, "
-                        f"{ring_words(desc)} pre-filled to 750, 4 frames per stream per step, bf16 "
+                        f"{ring_words(desc)}, pre-filled to 750 frames, 4 frames per stream per step, bf16 "
                         "N(0,1)*0.5, start positions U[1e4, 1e6)",
             "streams": S, "layers": 1, "frames_per_step": n, "heads": H, "head_dim": D,
             "window": W, "ring_slots": desc.ring_slots, "ring": args.ring,
@@ -247,7 +247,7 @@ def bench_c2(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": (measured_traffic("k_attn", "c2") or {}).get("bytes"),
+            "traffic": (measured_traffic("k_attn", workload_key(args, "c2")) or {}).get("bytes"),
             "alg_bytes_per_launch": nbytes[-1],
             "launch_us_mean": t_kernel * 1e6,
             "launches_timed": len(attn_ms),
@@ -265,6 +265,19 @@ def kernels_sha256() -> str:
     import hashlib
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def workload_key(args, name: str) -> str:
+    """Key of an encoder workload in profiles/hbm_traffic.txt: the config
+    name, with an m appended for the modulo-ring variant."""
+    return name + ("m" if getattr(args, "ring", "compact") == "mod" else "")
+
+
+def dec_traffic():
+    """Decoder step: split-K attention plus merge, per step."""
+    a = measured_traffic("k_attn_dec", "c4")
+    b = measured_traffic("k_dec_combine", "c4")
+    return a["bytes"] + b["bytes"] if a and b else None
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -392,7 +405,7 @@ def bench_c1(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": (measured_traffic("k_attn", workload_key(args, "c1")) or {}).get("bytes"),
             "alg_bytes_per_launch": nbytes[-1],
             "launch_us_mean": t_attn / len(attn_ms) * 1e6,
             "launches_timed": len(attn_ms),
@@ -501,7 +514,7 @@ def bench_c3(args):
             "peak": MFMA_BF16_PEAK_TFS,
             "unit": "TFLOP/s",
             "frac": tflops / MFMA_BF16_PEAK_TFS,
-            "traffic": (measured_traffic("k_attn_mfma", "c3") or {}).get("bytes"),
+            "traffic": (measured_traffic("k_attn_mfma", workload_key(args, "c3")) or {}).get("bytes"),
             "alg_flops_per_launch_full_window": full[0][1] if full else None,
             "launch_us_mean": t_attn / len(attn_ms) * 1e6,
             "launch_us_mean_full_window": (sum(a for a, _ in full) / len(full) * 1e3) if full else None,
@@ -627,7 +640,7 @@ def bench_c4(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": dec_traffic(),
             "alg_bytes_per_launch": nbytes[-1],
             "launch_us_mean": t_attn / len(attn_ms) * 1e6,
             "launches_timed": len(attn_ms),
