@@ -29,6 +29,11 @@ What it computes (sources are the four pages this method is described on):
                   plan page, "SHIPPED" section, "Unbounded length"
                   paragraph); decoder modulo ring, slot = pos % 8192 (family
                   doc, Streaming row, item 5).
+* ``block``     - the attention half of an encoder block around the path:
+                  RMSNorm, q/k/v projections with q and v biases, the
+                  windowed attention, the output projection with bias and the
+                  residual (family doc, "Architecture (summary)", Encoder
+                  bullet).
 * ``stream``    - the same attention driven incrementally through the ring
                   model with explicit fp64 ring buffers, feed by feed.  The
                   pages state the streamed result equals the offline pass
@@ -45,4 +50,4 @@ compaction counts in closed form; GQA = MHA with repeated kv heads; decoder
 modulo ring = linear buffer.  No output value of this oracle is "parity
 unpinned".
 """
-from . import rope, attention, ring, stream  # noqa: F401
+from . import rope, attention, ring, stream, block  # noqa: F401

@@ -74,6 +74,30 @@ def qkv(seed: int, stream: int, layer: int, T: int, hq: int, hkv: int, d: int,
     return q, k, v
 
 
+X = 3  # tensor id of an encoder block's input rows
+NORM_W, WQ, WK, WV, WO, BQ, BV, BO = range(10, 18)  # tensor ids of block weights
+
+
+def block_input(seed: int, stream: int, layer: int, T: int, dim: int, dtype: str = "bf16"):
+    """Block input rows x [T][dim], N(0,1)."""
+    return normal(seed, stream, layer, X, (T, dim), 1.0, dtype)
+
+
+def block_weights(seed: int, layer: int, dim: int, dtype: str = "bf16") -> dict:
+    """Random weights of one encoder attention block: norm gain 1 + 0.1 N(0,1),
+    projection matrices [out][in] N(0, 1/dim) (unit-variance outputs for
+    unit-variance inputs), biases 0.1 N(0,1).  Stream index 0x5EED1 keeps the
+    draws apart from any stream's activations."""
+    s = 0x5EED1
+    w = {"norm_w": 1.0 + normal(seed, s, layer, NORM_W, (dim,), 0.1, "f32")}
+    w["norm_w"] = round_to(w["norm_w"], dtype)
+    for name, tid in (("wq", WQ), ("wk", WK), ("wv", WV), ("wo", WO)):
+        w[name] = normal(seed, s, layer, tid, (dim, dim), dim ** -0.5, dtype)
+    for name, tid in (("bq", BQ), ("bv", BV), ("bo", BO)):
+        w[name] = normal(seed, s, layer, tid, (dim,), 0.1, dtype)
+    return w
+
+
 def offsets(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     """n integers uniform in [lo, hi) (start offsets, start positions or
     context lengths), from their own seed sequence."""
