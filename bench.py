@@ -17,6 +17,8 @@ c3            catch-up: 1 stream x 32 layers, bf16 N(0,1), 15300 frames fed as
               layers: compaction, RoPE + append, attention on the matrix
               cores.  The sequence restarts (host-only reset) after its last
               batch.
+c2b           the c2 step through the attention half of an encoder block
+              (RMSNorm, q/k/v projection, the path, output projection).
 c4            decoder step: 32 streams x 26 layers, GQA 32/8 x 128, window 8192.
 copy          calibration copy of 1 GiB for the HBM byte counters.
 
@@ -94,6 +96,43 @@ def cpu_baseline(streams: int, layers_in_config: int, pre: int, steps: int, n: i
                       f"(rings pre-filled with {pre} frames, not timed), oracle.stream.EncStream "
                       f"in fp64 numpy on one thread, {elapsed:.1f} s for {frame_layers} "
                       f"frame-layers, divided by {layers_in_config} layer(s) per frame"}
+
+
+def cpu_baseline_block(steps: int):
+    """The fp64 oracle through the attention half of a block, streamed: one
+    stream, rings pre-filled with 750 frames (not timed), then `steps` feeds
+    of 4 frames (timed): RMSNorm and projections (oracle.block) around
+    oracle.stream.EncStream."""
+    import numpy as np
+    from oracle import block
+    from oracle.stream import EncStream
+    from synth import block_input, block_weights
+
+    dim = H * D
+    wts = block_weights(5, 0, dim)
+    T = W + 4 * steps
+    x = block_input(5, 0, 0, T, dim)
+    st = EncStream(H, D, start_pos=12345)
+
+    def feed(xc):
+        y = block.rmsnorm(xc, wts["norm_w"])
+        q = block.linear(y, wts["wq"], wts["bq"]).reshape(-1, H, D)
+        k = block.linear(y, wts["wk"]).reshape(-1, H, D)
+        v = block.linear(y, wts["wv"], wts["bv"]).reshape(-1, H, D)
+        a = np.asarray(st.feed(q, k, v)).reshape(-1, dim)
+        return xc + block.linear(a, wts["wo"], wts["bo"])
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):   # one host thread, like the other oracle baselines
+        feed(x[:W])
+        t0 = time.perf_counter()
+        for i in range(steps):
+            feed(x[W + 4 * i:W + 4 * i + 4])
+        el = time.perf_counter() - t0
+    return {"value": 4 * steps / el, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"one stream x 1 layer, {steps} feeds of 4 frames through the block's attention "
+                      f"half (rings pre-filled with 750 frames, not timed), oracle.block + "
+                      f"oracle.stream.EncStream in fp64 numpy, {el:.1f} s"}
 
 
 def cpu_baseline_dec(contexts, steps: int = 20):
@@ -254,6 +293,126 @@ def bench_c2(args):
         },
         "compaction_steps": sum(compacting),
         "step_hbm_frac": sum(S * attn_work(k, n)[0] for k in nkv_seen) / wall / 1e9 / HBM_PEAK_GBS,
+    }
+
+
+def bench_c2b(args):
+    """The serving step of c2 through the whole attention half of an encoder
+    block: RMSNorm, the q/k/v projection (one GEMM, 1280 -> 3840, q and v
+    biases), the cached path, the output projection with bias and the
+    residual.  Random weights: gain 1 + 0.1 N(0,1), matrices N(0, 1/1280),
+    biases 0.1 N(0,1); inputs x ~ N(0,1); all bf16."""
+    import torch
+    import sliding_window_cached_amd as vrt
+    from synth import offsets
+
+    dev = torch.device("cuda:0")
+    S, n, dim = 256, 4, H * D
+    desc = enc_desc(args, 1)
+    starts = offsets(2, S, 10 ** 4, 10 ** 6)
+    nb = vrt.state_device_bytes(desc)
+    mem = torch.empty(S * nb, dtype=torch.uint8, device=dev)
+    states = [vrt.StreamState(desc, mem[i * nb:(i + 1) * nb], nb, int(starts[i])) for i in range(S)]
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    norm_w = (1.0 + 0.1 * torch.randn(dim, generator=gen, device=dev)).to(torch.bfloat16)
+    w_qkv = _randn(gen, (3 * dim, dim), dim ** -0.5, dev)
+    w_o = _randn(gen, (dim, dim), dim ** -0.5, dev)
+    b_q, b_v, b_o = (_randn(gen, (dim,), 0.1, dev) for _ in range(3))
+    bw = vrt.block_weights(norm_w, w_qkv, b_q, b_v, w_o, b_o, 1.0e-5)
+
+    log("c2b: pre-filling 256 rings to 750 frames through the block")
+    xp = _randn(gen, (S, W, dim), 1.0, dev)
+    wsb = vrt.block_workspace_bytes(desc, S * W)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    vrt.enc_block_feed(states, 0, xp, W, bw, torch.empty_like(xp), ws, wsb, stream)
+    torch.cuda.synchronize()
+    del xp, ws
+    total = args.warmup + args.steps
+    X = _randn(gen, (total, S, n, dim), 1.0, dev)
+    out = torch.empty((S, n, dim), dtype=torch.bfloat16, device=dev)
+    wsb = vrt.block_workspace_bytes(desc, S * n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        vrt.enc_block_feed(states, 0, X[i], n, bw, out, ws, wsb, stream)
+    torch.cuda.synchronize()
+    _, nkv = states[0].query(0)
+    nkv_seen = []
+    for i in range(args.steps):
+        _, nkv_after, _ = vrt.ring_advance(desc, 0, nkv, n)
+        nkv_seen.append(nkv_after - n)
+        nkv = nkv_after
+
+    every = max(1, args.timing_every)
+    timed = list(range(0, args.steps, every))
+    ev = dict(zip(timed, _timing_events(len(timed))))
+    blk = dict(zip(timed, _timing_events(len(timed))))
+    log(f"c2b: timing {args.steps} block steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        if j in ev:
+            vrt.set_attn_events(ev[j][0], ev[j][1])
+            blk[j][0].record()
+        elif every > 1 and j - 1 in ev:
+            vrt.set_attn_events()
+        vrt.enc_block_feed(states, 0, X[args.warmup + j], n, bw, out, ws, wsb, stream)
+        if j in blk:
+            blk[j][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    vrt.set_attn_events()
+    attn_ms = [ev[j][0].elapsed_time(ev[j][1]) for j in timed]
+    blk_ms = [blk[j][0].elapsed_time(blk[j][1]) for j in timed]
+    for st in states:
+        st.close()
+    M = S * n
+    proj_flops = 2 * M * dim * (3 * dim) + 2 * M * dim * dim
+    nbytes = [S * attn_work(nkv_seen[j], n)[0] for j in timed]
+    t_attn = sum(attn_ms) * 1e-3 / len(attn_ms)
+    t_blk = sum(blk_ms) * 1e-3 / len(blk_ms)
+    achieved = sum(nbytes) / (sum(attn_ms) * 1e-3) / 1e9
+    return {
+        "metric": "encoder frames/s through the attention half of a block (norm, projections, "
+                  "cached window-750 attention, output projection; all streams)",
+        "value": S * n * args.steps / wall,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random weights)",
+        "config": {
+            "workload": f"serving step through the attention half of an encoder block: 256 streams x "
+                        f"1 layer, d_model 1280 = 20 heads x 64, window 750, {ring_words(desc)}, "
+                        "pre-filled to 750 frames, 4 frames per stream per step, x ~ N(0,1), "
+                        "random weights, bf16",
+            "streams": S, "layers": 1, "frames_per_step": n, "d_model": dim, "window": W,
+            "ring_slots": desc.ring_slots, "ring": args.ring, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_attn (the cached path inside the block)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": (measured_traffic("k_attn", workload_key(args, "c2")) or {}).get("bytes"),
+            "launch_us_mean": t_attn * 1e6,
+            "launches_timed": len(attn_ms),
+        },
+        "block": {
+            "us_mean": t_blk * 1e6,
+            "attention_us_mean": t_attn * 1e6,
+            "norm_and_projections_us_mean": (t_blk - t_attn) * 1e6,
+            "projection_flops_per_step": proj_flops,
+            "projection_tflops_incl_norm": proj_flops / (t_blk - t_attn) / 1e12,
+        },
     }
 
 
@@ -653,7 +812,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "copy"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2b", "c3", "c4", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ring", default="compact", choices=["compact", "mod"],
                     help="encoder configs: compacting ring (the pages') or modulo ring")
@@ -674,6 +833,10 @@ def main():
         args.steps = 1000 if args.steps is None else args.steps
         args.warmup = 20 if args.warmup is None else args.warmup
         res = bench_c2(args)
+    elif args.config == "c2b":
+        args.steps = 300 if args.steps is None else args.steps
+        args.warmup = 10 if args.warmup is None else args.warmup
+        res = bench_c2b(args)
     elif args.config == "c1":
         args.steps = 200 if args.steps is None else args.steps
         args.warmup = 10 if args.warmup is None else args.warmup
@@ -694,6 +857,8 @@ def main():
         if args.config == "c2":
             res["cpu_baseline"] = cpu_baseline(1, 1, W, 400, 4, 0.5, offsets(2, 1, 10 ** 4, 10 ** 6),
                                                "steady-state sample")
+        elif args.config == "c2b":
+            res["cpu_baseline"] = cpu_baseline_block(60)
         elif args.config == "c1":
             res["cpu_baseline"] = cpu_baseline(1, 32, W, 400, 4, 0.5, [0], "staggered-streams sample")
         elif args.config == "c3":

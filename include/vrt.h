@@ -235,6 +235,61 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* states, int n_states, int 
                              int n_tok, void* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* ---- The attention half of an encoder block around the path (family doc,
+ * "Architecture (summary)", Encoder bullet: pre-norm RMSNorm blocks, NEOX
+ * RoPE, the causal 750-frame sliding window, biases on q, v and o and none on
+ * k).  bf16 storage throughout, fp32 accumulation; every intermediate is
+ * rounded to bf16 once, where it is stored. */
+
+/* y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w, row by row: x, y [rows][dim],
+ * w [dim], bf16, 16-byte aligned; dim a multiple of 8 and at most 2048.
+ * Computed in fp32 with one rounding.  VRT_ERR_INVALID on bad sizes,
+ * pointers, alignment or eps (negative or not finite). */
+vrt_status vrt_rmsnorm(const void* x, int rows, int dim, const void* w, float eps, void* y,
+                       hipStream_t stream);
+
+/* out = A W^T (+ bias) (+ residual): A [M][K], W [N][K] (one row per output
+ * column, a projection matrix as stored), bias [N] or null, residual [M][N]
+ * or null, out [M][N]; bf16, fp32 accumulation on the matrix cores, one
+ * rounding.  A and W 16-byte aligned.  VRT_ERR_UNSUPPORTED unless K is a
+ * multiple of 64 and N a multiple of 128; VRT_ERR_INVALID on null or
+ * misaligned pointers or M < 1.  out must not overlap A, W or residual. */
+vrt_status vrt_linear(const void* A, int M, int K, const void* W, int N, const void* bias,
+                      const void* residual, void* out, hipStream_t stream);
+
+/* Weights of one block's attention half, device pointers, bf16, with
+ * dim = n_heads * head_dim features in head-major order. */
+typedef struct {
+    const void* norm_w;  /* [dim] RMSNorm gain */
+    const void* w_qkv;   /* [3 * dim][dim]: the rows of Wq, then Wk, then Wv */
+    const void* b_q;     /* [dim] or null */
+    const void* b_v;     /* [dim] or null (k has no bias) */
+    const void* w_o;     /* [dim][dim] */
+    const void* b_o;     /* [dim] or null */
+    float eps;           /* RMSNorm epsilon (the pages print none; 1e-5 is usual) */
+    int32_t reserved;    /* must be 0 */
+} vrt_block_weights;
+
+/* Workspace of vrt_enc_block_feed for n_rows = n_states * n_new rows: the
+ * normed rows, q, k, v and the attention output, bf16, each 256-byte
+ * aligned.  0 for an invalid desc or n_rows < 1. */
+size_t vrt_block_workspace_bytes(const vrt_cache_desc* desc, int n_rows);
+
+/* One feed through the attention half of layer `layer` of each state:
+ *   y = RMSNorm(x); q = y Wq^T + b_q; k = y Wk^T; v = y Wv^T + b_v;
+ *   a = the cached path (vrt_enc_attn_feed with q, k, v, one layer);
+ *   out = x + a Wo^T + b_o.
+ * x/out: [n_states][n_new][dim].  Encoder states (either ring kind) with
+ * bf16 storage and n_heads_q == n_heads_kv; dim a multiple of 128 and at
+ * most 2048.  Every check of vrt_enc_attn_feed is made before anything is
+ * enqueued, plus VRT_ERR_INVALID for null or misaligned (16-byte) pointers,
+ * a nonzero reserved field or eps < 0, VRT_ERR_CAPACITY for a short
+ * workspace, VRT_ERR_UNSUPPORTED for other storage or head layouts.
+ * The states advance exactly as under vrt_enc_attn_feed. */
+vrt_status vrt_enc_block_feed(vrt_stream_state* const* states, int n_states, int layer,
+                              const void* x, int n_new, const vrt_block_weights* w, void* out,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Per-component timing (the pages time each stage of a streamed feed on its
  * own: family doc, Capability Validation table, Streaming row, items 7 and
  * 8).  While both events are non-null, every later call on this thread

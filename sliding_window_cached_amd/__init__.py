@@ -29,7 +29,15 @@ EXPORTS = (
     "vrt_stream_state_destroy", "vrt_stream_state_query", "vrt_ring_advance", "vrt_attn_path",
     "vrt_offline_scratch_bytes", "vrt_enc_attn_offline", "vrt_enc_attn_feed",
     "vrt_ring_compact", "vrt_dec_workspace_bytes", "vrt_dec_attn_step", "vrt_set_attn_events",
+    "vrt_rmsnorm", "vrt_linear", "vrt_block_workspace_bytes", "vrt_enc_block_feed",
 )
+
+
+class BlockWeights(Structure):
+    """vrt_block_weights: device pointers of one block's attention half."""
+    _fields_ = [("norm_w", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("b_q", ctypes.c_void_p),
+                ("b_v", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("b_o", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("reserved", c_int32)]
 
 
 class CacheDesc(Structure):
@@ -123,6 +131,11 @@ def _load():
         "vrt_dec_attn_step": (c_int, [POINTER(P), c_int, c_int, c_int, P, P, P, c_int, P, P,
                                       c_size_t, P]),
         "vrt_set_attn_events": (c_int, [P, P]),
+        "vrt_rmsnorm": (c_int, [P, c_int, c_int, P, ctypes.c_float, P, P]),
+        "vrt_linear": (c_int, [P, c_int, c_int, P, c_int, P, P, P, P]),
+        "vrt_block_workspace_bytes": (c_size_t, [POINTER(CacheDesc), c_int]),
+        "vrt_enc_block_feed": (c_int, [POINTER(P), c_int, c_int, P, c_int, POINTER(BlockWeights), P,
+                                       P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -253,6 +266,39 @@ def dec_attn_step(states, layer0, n_layers, q, k, v, n_tok, out, workspace=None,
                               _ptr(v), n_tok, _ptr(out), _ptr(workspace), ws_bytes, stream)
     if check:
         _check(s, "dec_attn_step")
+    return s
+
+
+def rmsnorm(x, rows, dim, w, eps, y, stream=0, check=True):
+    s = lib.vrt_rmsnorm(_ptr(x), rows, dim, _ptr(w), eps, _ptr(y), stream)
+    if check:
+        _check(s, "rmsnorm")
+    return s
+
+
+def linear(A, M, K, W, N, bias, residual, out, stream=0, check=True):
+    s = lib.vrt_linear(_ptr(A), M, K, _ptr(W), N, _ptr(bias), _ptr(residual), _ptr(out), stream)
+    if check:
+        _check(s, "linear")
+    return s
+
+
+def block_weights(norm_w, w_qkv, b_q, b_v, w_o, b_o, eps=1.0e-5) -> BlockWeights:
+    """Keep the owners (e.g. torch tensors) alive while the struct is used."""
+    return BlockWeights(_ptr(norm_w), _ptr(w_qkv), _ptr(b_q), _ptr(b_v), _ptr(w_o), _ptr(b_o),
+                        eps, 0)
+
+
+def block_workspace_bytes(desc, n_rows) -> int:
+    return lib.vrt_block_workspace_bytes(byref(desc), n_rows)
+
+
+def enc_block_feed(states, layer, x, n_new, weights: BlockWeights, out, workspace, ws_bytes,
+                   stream=0, check=True):
+    s = lib.vrt_enc_block_feed(_handles(states), len(states), layer, _ptr(x), n_new, byref(weights),
+                               _ptr(out), _ptr(workspace), ws_bytes, stream)
+    if check:
+        _check(s, "enc_block_feed")
     return s
 
 

@@ -1,0 +1,277 @@
+// vrt_block.hip - the kernels of the encoder attention block around the
+// cached path (family doc, "Architecture (summary)", Encoder bullet: pre-norm
+// RMSNorm blocks, attention with q, v and o biases and none on k):
+//
+//   k_rmsnorm : y = x / sqrt(mean(x^2) + eps) * w, one workgroup per row
+//   k_gemm    : out = A W^T (+ bias) (+ residual), bf16 operands on the matrix
+//               cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation, one
+//               rounding to bf16 at the end
+//
+// Both are plain dense work: the GEMM is a contraction (matrix cores), the
+// norm a row reduction (one pass over HBM).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "vrt_internal.h"
+
+namespace vrt {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// 16 bytes per lane, HBM -> LDS (global_load_lds_dwordx4: lane i writes bytes
+// [16i, 16i + 16) after the wave-uniform LDS address in M0).  Inline asm, so
+// the compiler does not tie its own LDS reads to these writes; every read of
+// a stage is ordered after its DMA by wait_vm and a workgroup barrier.  M0 is
+// saved and restored around the instruction, with the one wait state an M0
+// write needs before an LDS DMA.
+__device__ __forceinline__ void dma16(const char* g, char* l) {
+    const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(__UINTPTR_TYPE__)l);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"((unsigned long long)(__UINTPTR_TYPE__)g), "s"(lds)
+        : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// ------------------------------------------------------------ RMSNorm ----
+// One workgroup of 256 threads per row; thread c holds features 8c .. 8c+7
+// (dim % 8 == 0, dim <= 2048).  Sum of squares in fp32: per thread in feature
+// order, then the 64 lanes of a wave by a butterfly, then the 4 waves in
+// order, so the result is fixed for a given row.  y = bf16((x * rstd) * w).
+__global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
+    __shared__ float part[4];
+    const int row = blockIdx.x, c = threadIdx.x;
+    const bool on = 8 * c < a.dim;
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    if (on) xv = *(const uint4*)((const char*)a.x + ((long long)row * a.ldx + 8 * c) * 2);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = bf_lo(xw[i]), hi = bf_hi(xw[i]);
+        s = __fmaf_rn(lo, lo, s);
+        s = __fmaf_rn(hi, hi, s);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+    if ((c & 63) == 0) part[c >> 6] = s;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float rstd = 1.0f / sqrtf(tot / (float)a.dim + a.eps);
+    if (!on) return;
+    const uint4 wv = *(const uint4*)((const char*)a.w + 16 * c);
+    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    uint32_t yw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        yw[i] = pack2((bf_lo(xw[i]) * rstd) * bf_lo(ww[i]), (bf_hi(xw[i]) * rstd) * bf_hi(ww[i]));
+    *(uint4*)((char*)a.y + ((long long)row * a.ldy + 8 * c) * 2) = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+}
+
+// --------------------------------------------------------------- GEMM ----
+// out[m][n] = sum_k A[m][k] W[n][k] (+ bias[n]) (+ R[m][n]), A and W bf16
+// row-major (W has one row per output feature, as a projection matrix).
+// Workgroup tile BM x BN, k step 64; 4 waves in a 2 x 2 grid, wave (wm, wn)
+// owning rows wm BM/2 .. and columns wn BN/2 .. as (BM/64) x (BN/64) blocks of
+// 32 x 32.  With the 32x32x16 operand layouts (A lane l: row l % 32, k
+// 8 (l / 32) .. +7; B lane l: column l % 32, the same k) both operands are
+// read the same way from row-major tiles: one 16-byte LDS read per lane per
+// block and k16 step.  Tiles go HBM -> LDS by DMA through NST stages (NST - 1
+// in flight while one is read); rows are 128 bytes, their 16-byte chunks
+// XOR-swizzled by (row / 2) mod 8, so the 32 rows read together hit distinct
+// banks.  Rows of A past M are fetched from row M - 1 and never stored.  The
+// k order of every output element is the same for every tile shape, so the
+// shape changes no result.
+template <int BM_, int BN_, int NST_>
+struct GT {
+    static constexpr int BM = BM_, BN = BN_, BK = 64, NST = NST_;
+    static constexpr int RB = BK * 2;               // bytes per tile row
+    static constexpr int ATILE = BM * RB, WTILE = BN * RB;
+    static constexpr int STAGE = ATILE + WTILE;
+    static constexpr int AIPW = ATILE / 1024 / 4;   // DMA instructions per wave per A tile
+    static constexpr int WIPW = WTILE / 1024 / 4;
+    static constexpr int LPW = AIPW + WIPW;         // per stage
+    static constexpr int IB = BM / 64, JB = BN / 64;  // 32 x 32 blocks per wave
+    static constexpr int BYTES = NST * STAGE;
+};
+__device__ __forceinline__ int gsw(int r) { return (r >> 1) & 7; }
+
+template <class L>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int ntn = a.N / L::BN;
+    const int m0 = (blockIdx.x / ntn) * L::BM, n0 = (blockIdx.x % ntn) * L::BN;
+    const int nk = a.K / L::BK;
+    const char* A = (const char*)a.A;
+    const char* W = (const char*)a.W;
+
+    auto issue = [&](int kt, int st) {
+        char* as = lds + st * L::STAGE;
+        char* ws = as + L::ATILE;
+        const long long kb = (long long)kt * L::BK * 2;
+#pragma unroll
+        for (int i = 0; i < L::AIPW; ++i) {
+            const int ins = wave * L::AIPW + i;
+            const int q = ins * 64 + lane;          // 16-byte chunk of the tile this lane fills
+            const int r = q >> 3, c = (q & 7) ^ gsw(r);
+            const int ra = min(m0 + r, a.M - 1);
+            dma16(A + (long long)ra * a.lda * 2 + kb + 16 * c, as + ins * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < L::WIPW; ++i) {
+            const int ins = wave * L::WIPW + i;
+            const int q = ins * 64 + lane;
+            const int r = q >> 3, c = (q & 7) ^ gsw(r);
+            dma16(W + (long long)(n0 + r) * a.ldw * 2 + kb + 16 * c, ws + ins * 1024);
+        }
+    };
+
+    f32x16_t acc[L::IB][L::JB];
+#pragma unroll
+    for (int i = 0; i < L::IB; ++i)
+#pragma unroll
+        for (int j = 0; j < L::JB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // lane parts of the operand reads: row l % 32 of each block, chunk
+    // 2 * k16 + l / 32 (swizzled by the row)
+    const int lr = lane & 31, hf = lane >> 5;
+    int aoff[L::IB][4], woff[L::JB][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int i = 0; i < L::IB; ++i) {
+            const int ra = (L::BM / 2) * wm + 32 * i + lr;
+            aoff[i][s] = ra * L::RB + 16 * ((2 * s + hf) ^ gsw(ra));
+        }
+#pragma unroll
+        for (int j = 0; j < L::JB; ++j) {
+            const int rw = (L::BN / 2) * wn + 32 * j + lr;
+            woff[j][s] = L::ATILE + rw * L::RB + 16 * ((2 * s + hf) ^ gsw(rw));
+        }
+    }
+
+#pragma unroll
+    for (int st = 0; st < L::NST - 1; ++st)
+        if (st < nk) issue(st, st);
+    for (int kt = 0; kt < nk; ++kt) {
+        // outstanding: tiles kt .. min(kt + NST - 2, nk - 1), issued in order
+        const int after = min(L::NST - 2, nk - 1 - kt);   // tiles issued after tile kt
+        if constexpr (L::NST >= 4) {
+            if (after >= 2) wait_vm<2 * L::LPW>();
+            else if (after == 1) wait_vm<L::LPW>();
+            else wait_vm<0>();
+        } else {
+            if (after >= 1) wait_vm<L::LPW>(); else wait_vm<0>();
+        }
+        __syncthreads();   // tile kt landed for every wave; tile kt - 1's stage is free
+        if (kt + L::NST - 1 < nk) issue(kt + L::NST - 1, (kt + L::NST - 1) % L::NST);
+        const char* S = lds + (kt % L::NST) * L::STAGE;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8_t av[L::IB], wv[L::JB];
+#pragma unroll
+            for (int i = 0; i < L::IB; ++i)
+                av[i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(S + aoff[i][s]));
+#pragma unroll
+            for (int j = 0; j < L::JB; ++j)
+                wv[j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(S + woff[j][s]));
+#pragma unroll
+            for (int i = 0; i < L::IB; ++i)
+#pragma unroll
+                for (int j = 0; j < L::JB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], wv[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // epilogue: lane l, register r of block (i, j) holds row
+    // 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32 of the block
+    const int seg = n0 / a.seg_w;
+    char* out = (char*)a.seg[seg].out;
+    const char* bias = (const char*)a.seg[seg].bias;
+    const long long ldo = a.seg[seg].ld;
+#pragma unroll
+    for (int j = 0; j < L::JB; ++j) {
+        const int col = n0 + (L::BN / 2) * wn + 32 * j + lr;
+        const int lc = col - seg * a.seg_w;
+        const float bv = bias ? __uint_as_float((uint32_t)*(const uint16_t*)(bias + 2 * lc) << 16) : 0.f;
+#pragma unroll
+        for (int i = 0; i < L::IB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + (L::BM / 2) * wm + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
+                if (row >= a.M) continue;
+                float v = acc[i][j][r] + bv;
+                if (a.R)
+                    v += __uint_as_float(
+                        (uint32_t)*(const uint16_t*)((const char*)a.R + ((long long)row * a.ldr + col) * 2) << 16);
+                *(uint16_t*)(out + ((long long)row * ldo + lc) * 2) = to_bf16(v);
+            }
+    }
+}
+
+// Tile shapes, largest first: 128 x 128 with 3 tiles in flight (one
+// workgroup per CU), 64 x 128 and 64 x 64 with 2 and 3 in flight (two per
+// CU).  For few rows the products are bound by the bytes of re-read tiles
+// at the loaded memory latency, not by the matrix cores; smaller tiles fill
+// more CUs.
+using G128 = GT<128, 128, 4>;
+using G64x128 = GT<64, 128, 3>;
+using G64 = GT<64, 64, 4>;
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s) {
+    if (a.rows < 1 || a.dim < 8 || a.dim % 8 != 0 || a.dim > 2048) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+    if (a.M < 1 || a.N < 128 || a.N % 128 != 0 || a.K < 64 || a.K % 64 != 0 || a.seg_w < 128 ||
+        a.seg_w % 128 != 0 || a.N != a.seg_w * a.n_seg || a.n_seg < 1 || a.n_seg > kMaxGemmSeg)
+        return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    // the largest tile that still gives every CU a workgroup
+    const long long t128 = (long long)((a.M + 127) / 128) * (a.N / 128);
+    const long long t64x128 = (long long)((a.M + 63) / 64) * (a.N / 128);
+    const long long t64 = (long long)((a.M + 63) / 64) * (a.N / 64);
+    if (t64 > INT32_MAX) return hipErrorInvalidValue;   // (t128 <= t64x128 <= t64)
+    if (t128 >= cus)
+        hipLaunchKernelGGL(k_gemm<G128>, dim3((unsigned)t128), dim3(256), 0, s, a);
+    else if (t64x128 >= cus)
+        hipLaunchKernelGGL(k_gemm<G64x128>, dim3((unsigned)t64x128), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_gemm<G64>, dim3((unsigned)t64), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace vrt

@@ -660,4 +660,115 @@ vrt_status vrt_set_attn_events(hipEvent_t start, hipEvent_t stop) {
     return VRT_OK;
 }
 
+
+// ---- encoder attention block around the path
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+vrt_status vrt_rmsnorm(const void* x, int rows, int dim, const void* w, float eps, void* y,
+                       hipStream_t stream) {
+    if (!x || !w || !y || rows < 1 || dim < 8 || dim % 8 != 0 || dim > 2048) return VRT_ERR_INVALID;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return VRT_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return VRT_ERR_INVALID;
+    NormArgs a{x, dim, w, y, dim, rows, dim, eps};
+    clear_sticky_error();
+    return note(launch_rmsnorm(a, stream)) == hipSuccess ? VRT_OK : VRT_ERR_DEVICE;
+}
+
+vrt_status vrt_linear(const void* A, int M, int K, const void* W, int N, const void* bias,
+                      const void* residual, void* out, hipStream_t stream) {
+    if (!A || !W || !out || M < 1 || K < 1 || N < 1) return VRT_ERR_INVALID;
+    if (K % 64 != 0 || N % 128 != 0) return VRT_ERR_UNSUPPORTED;
+    if (!aligned16(A) || !aligned16(W) || ((uintptr_t)out & 1) || ((uintptr_t)bias & 1) ||
+        ((uintptr_t)residual & 1))
+        return VRT_ERR_INVALID;
+    GemmArgs g{};
+    g.A = A;
+    g.lda = K;
+    g.W = W;
+    g.ldw = K;
+    g.R = residual;
+    g.ldr = N;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.seg_w = N;
+    g.n_seg = 1;
+    g.seg[0] = GemmSeg{out, bias, N};
+    clear_sticky_error();
+    return note(launch_gemm(g, stream)) == hipSuccess ? VRT_OK : VRT_ERR_DEVICE;
+}
+
+static size_t block_buf_bytes(int n_rows, int dim) {
+    return ((size_t)n_rows * dim * 2 + 255) / 256 * 256;
+}
+
+size_t vrt_block_workspace_bytes(const vrt_cache_desc* desc, int n_rows) {
+    if (check_desc(desc) != VRT_OK || n_rows < 1) return 0;
+    return 5 * block_buf_bytes(n_rows, desc->n_heads_q * desc->head_dim);
+}
+
+vrt_status vrt_enc_block_feed(vrt_stream_state* const* st, int n_states, int layer, const void* x,
+                              int n_new, const vrt_block_weights* w, void* out, void* workspace,
+                              size_t ws_bytes, hipStream_t stream) {
+    if (!st || n_states < 1 || !st[0] || !is_encoder(st[0]->d)) return VRT_ERR_INVALID;
+    vrt_status s = check_batch(st, n_states, layer, 1, st[0]->d.kind);
+    if (s != VRT_OK) return s;
+    const vrt_cache_desc& d = st[0]->d;
+    if (!x || !out || !w || !workspace || n_new < 1) return VRT_ERR_INVALID;
+    if (!w->norm_w || !w->w_qkv || !w->w_o || w->reserved != 0) return VRT_ERR_INVALID;
+    if (!(w->eps >= 0.f) || !std::isfinite(w->eps)) return VRT_ERR_INVALID;
+    if (d.dtype != VRT_BF16 || d.n_heads_q != d.n_heads_kv) return VRT_ERR_UNSUPPORTED;
+    const int dim = d.n_heads_q * d.head_dim;
+    if (dim % 128 != 0 || dim > 2048) return VRT_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace) || !aligned16(w->norm_w) ||
+        !aligned16(w->w_qkv) || !aligned16(w->w_o) || ((uintptr_t)w->b_q & 1) ||
+        ((uintptr_t)w->b_v & 1) || ((uintptr_t)w->b_o & 1))
+        return VRT_ERR_INVALID;
+    if ((long long)n_states * n_new > INT_MAX / 4) return VRT_ERR_INVALID;
+    const int M = n_states * n_new;
+    if (ws_bytes < vrt_block_workspace_bytes(&d, M)) return VRT_ERR_CAPACITY;
+    // the checks vrt_enc_attn_feed makes, before anything is enqueued
+    for (int i = 0; i < n_states; ++i)
+        if (st[i]->abs_base[layer] + st[i]->n_kv[layer] > kPosLimit - n_new) return VRT_ERR_INVALID;
+
+    const size_t bb = block_buf_bytes(M, dim);
+    char* ws = (char*)workspace;
+    char *y = ws, *q = ws + bb, *k = ws + 2 * bb, *v = ws + 3 * bb, *a = ws + 4 * bb;
+    clear_sticky_error();
+    NormArgs na{x, dim, w->norm_w, y, dim, M, dim, w->eps};
+    if (note(launch_rmsnorm(na, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    GemmArgs g{};
+    g.A = y;
+    g.lda = dim;
+    g.W = w->w_qkv;
+    g.ldw = dim;
+    g.M = M;
+    g.N = 3 * dim;
+    g.K = dim;
+    g.seg_w = dim;
+    g.n_seg = 3;
+    g.seg[0] = GemmSeg{q, w->b_q, dim};
+    g.seg[1] = GemmSeg{k, nullptr, dim};
+    g.seg[2] = GemmSeg{v, w->b_v, dim};
+    if (note(launch_gemm(g, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    s = vrt_enc_attn_feed(st, n_states, layer, 1, q, k, v, n_new, a, stream);
+    if (s != VRT_OK) return s;
+    GemmArgs o{};
+    o.A = a;
+    o.lda = dim;
+    o.W = w->w_o;
+    o.ldw = dim;
+    o.R = x;
+    o.ldr = dim;
+    o.M = M;
+    o.N = dim;
+    o.K = dim;
+    o.seg_w = dim;
+    o.n_seg = 1;
+    o.seg[0] = GemmSeg{out, w->b_o, dim};
+    if (note(launch_gemm(o, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    return VRT_OK;
+}
+
 }  // extern "C"

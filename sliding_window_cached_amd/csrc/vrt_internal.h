@@ -106,6 +106,38 @@ struct CompactArgs {
     int kept;           // rows kept (= window)
 };
 
+// ---- encoder attention block around the path (vrt_block.hip)
+struct NormArgs {
+    const void* x;      // [rows][ldx] bf16
+    long long ldx;
+    const void* w;      // [dim] bf16 gain
+    void* y;            // [rows][ldy] bf16
+    long long ldy;
+    int rows, dim;
+    float eps;
+};
+
+constexpr int kMaxGemmSeg = 4;
+struct GemmSeg {
+    void* out;          // [M][ld] bf16: columns [s * seg_w, (s + 1) * seg_w) of the product
+    const void* bias;   // [seg_w] bf16 or null
+    long long ld;
+};
+struct GemmArgs {
+    const void* A;      // [M][lda] bf16
+    long long lda;
+    const void* W;      // [N][ldw] bf16, one row per output column
+    long long ldw;
+    const void* R;      // [M][ldr] bf16 residual added to every column, or null
+    long long ldr;
+    int M, N, K;
+    int seg_w, n_seg;
+    GemmSeg seg[kMaxGemmSeg];
+};
+
+hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
 hipError_t launch_rope_append(const AppendArgs& a, const StateTable& t, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t s);

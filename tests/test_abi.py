@@ -245,3 +245,36 @@ def test_modulo_encoder_ring_host_rules():
     assert vrt.enc_attn_feed([top], 0, 1, P, P, P, 4, P, 0, check=False) == vrt.ERR_INVALID
     with pytest.raises(vrt.VrtError):
         vrt.ring_advance(vrt.enc_desc(kind=M), lim - 3, 0, 4)
+
+
+def test_block_entry_argument_checks():
+    """vrt_rmsnorm / vrt_linear / vrt_enc_block_feed refuse bad arguments
+    before anything is enqueued (no GPU work here)."""
+    P = FAKE
+    assert vrt.rmsnorm(P, 0, 1280, P, 1e-5, P, check=False) == vrt.ERR_INVALID
+    assert vrt.rmsnorm(P, 4, 1284, P, 1e-5, P, check=False) == vrt.ERR_INVALID     # dim % 8
+    assert vrt.rmsnorm(P, 4, 4096, P, 1e-5, P, check=False) == vrt.ERR_INVALID     # > 2048
+    assert vrt.rmsnorm(P + 8, 4, 1280, P, 1e-5, P, check=False) == vrt.ERR_INVALID  # alignment
+    assert vrt.rmsnorm(P, 4, 1280, P, -1.0, P, check=False) == vrt.ERR_INVALID
+    assert vrt.linear(P, 4, 1280, P, 1300, None, None, P, check=False) == vrt.ERR_UNSUPPORTED
+    assert vrt.linear(P, 4, 100, P, 1280, None, None, P, check=False) == vrt.ERR_UNSUPPORTED
+    assert vrt.linear(P, 0, 1280, P, 1280, None, None, P, check=False) == vrt.ERR_INVALID
+    assert vrt.linear(None, 4, 1280, P, 1280, None, None, P, check=False) == vrt.ERR_INVALID
+    d = vrt.enc_desc()
+    st = _state(d)
+    bw = vrt.block_weights(P, P, P, P, P, P)
+    assert vrt.block_workspace_bytes(d, 8) == 5 * 8 * 1280 * 2
+    ws = vrt.block_workspace_bytes(d, 4)      # one state, 4 frames
+    assert vrt.enc_block_feed([st], 0, P, 4, bw, P, P, ws - 1, check=False) == vrt.ERR_CAPACITY
+    assert vrt.enc_block_feed([st], 1, P, 4, bw, P, P, ws, check=False) == vrt.ERR_INVALID   # layer
+    assert vrt.enc_block_feed([st], 0, None, 4, bw, P, P, ws, check=False) == vrt.ERR_INVALID
+    bad = vrt.block_weights(P, P, P, P, P, P)
+    bad.reserved = 1
+    assert vrt.enc_block_feed([st], 0, P, 4, bad, P, P, ws, check=False) == vrt.ERR_INVALID
+    f32 = _state(vrt.enc_desc(dtype=vrt.F32))
+    assert vrt.enc_block_feed([f32], 0, P, 4, bw, P, P, ws, check=False) == vrt.ERR_UNSUPPORTED
+    dec = _state(vrt.dec_desc())
+    assert vrt.enc_block_feed([dec], 0, P, 1, bw, P, P, ws, check=False) == vrt.ERR_INVALID
+    top = _state(d, 2 ** 31 - 3)
+    assert vrt.enc_block_feed([top], 0, P, 4, bw, P, P, ws, check=False) == vrt.ERR_INVALID
+    assert st.query(0) == (0, 0) and top.query(0) == (2 ** 31 - 3, 0)
