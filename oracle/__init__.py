@@ -34,6 +34,10 @@ What it computes (sources are the four pages this method is described on):
                   windowed attention, the output projection with bias and the
                   residual (family doc, "Architecture (summary)", Encoder
                   bullet).
+* ``conv``      - the causal conv stem ahead of the encoder (kernel 3, strides
+                  1 and 2, left padding 2 and 1, GELU), offline and streamed
+                  with padding caches (family doc, Encoder bullet;
+                  streaming-plan page, "Chunk alignment").
 * ``stream``    - the same attention driven incrementally through the ring
                   model with explicit fp64 ring buffers, feed by feed.  The
                   pages state the streamed result equals the offline pass
@@ -50,4 +54,4 @@ compaction counts in closed form; GQA = MHA with repeated kv heads; decoder
 modulo ring = linear buffer.  No output value of this oracle is "parity
 unpinned".
 """
-from . import rope, attention, ring, stream, block  # noqa: F401
+from . import rope, attention, ring, stream, block, conv  # noqa: F401
