@@ -20,6 +20,7 @@ c3            catch-up: 1 stream x 32 layers, bf16 N(0,1), 15300 frames fed as
 c2b           the c2 step through the attention half of an encoder block
               (RMSNorm, q/k/v projection, the path, output projection).
 c4            decoder step: 32 streams x 26 layers, GQA 32/8 x 128, window 8192.
+cs            the causal conv stem: 256 streams x 8 mel frames per step.
 copy          calibration copy of 1 GiB for the HBM byte counters.
 
 --ring mod runs c1, c2 or c3 with the encoder cache kept as a modulo ring
@@ -414,6 +415,109 @@ def bench_c2b(args):
             "projection_tflops_incl_norm": proj_flops / (t_blk - t_attn) / 1e12,
         },
     }
+
+
+def bench_cs(args):
+    """The conv stem at the serving shape: 256 streams, 8 new mel frames per
+    stream per step (the pages' chunk), 128 mel bins -> 1280, giving 4
+    encoder frames per stream per step.  Random weights N(0, 1/fan_in),
+    biases 0.1 N(0,1), mel ~ N(0,1); bf16."""
+    import torch
+    import sliding_window_cached_amd as vrt
+
+    dev = torch.device("cuda:0")
+    S, n, n_mel, d = 256, 8, 128, H * D
+    nb = vrt.conv_stem_device_bytes(n_mel, d)
+    mem = torch.empty(S * nb, dtype=torch.uint8, device=dev)
+    stems = [vrt.ConvStem(n_mel, d, mem[i * nb:(i + 1) * nb], nb) for i in range(S)]
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    w0 = _randn(gen, (d, 3 * n_mel), (3 * n_mel) ** -0.5, dev)
+    w1 = _randn(gen, (d, 3 * d), (3 * d) ** -0.5, dev)
+    b0, b1 = (_randn(gen, (d,), 0.1, dev) for _ in range(2))
+    cw = vrt.conv_weights(w0, b0, w1, b1)
+    total = args.warmup + args.steps
+    mel = _randn(gen, (total, S, n, n_mel), 1.0, dev)
+    out = torch.empty((S, n // 2, d), dtype=torch.bfloat16, device=dev)
+    wsb = vrt.conv_workspace_bytes(n_mel, d, S, n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        vrt.conv_stem_feed(stems, mel[i], n, cw, out, ws, wsb, stream)
+    torch.cuda.synchronize()
+    every = max(1, args.timing_every)
+    timed = list(range(0, args.steps, every))
+    ev = dict(zip(timed, _timing_events(len(timed))))
+    log(f"cs: timing {args.steps} conv stem steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        if j in ev:
+            ev[j][0].record()
+        vrt.conv_stem_feed(stems, mel[args.warmup + j], n, cw, out, ws, wsb, stream)
+        if j in ev:
+            ev[j][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[j][0].elapsed_time(ev[j][1]) for j in timed]
+    for st in stems:
+        st.close()
+    t_step = sum(ms) * 1e-3 / len(ms)
+    flops = 2 * S * n * d * 3 * n_mel + 2 * S * (n // 2) * d * 3 * d
+    tfs = flops / t_step / 1e12
+    return {
+        "metric": "encoder frames/s out of the causal conv stem (all streams)",
+        "value": S * (n // 2) * args.steps / wall,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random weights)",
+        "config": {
+            "workload": "conv stem serving step: 256 streams, 8 new mel frames each (128 bins), conv "
+                        "128 -> 1280 k3 s1 and 1280 -> 1280 k3 s2 with bias and GELU, padding caches; "
+                        "4 encoder frames per stream per step",
+            "streams": S, "mel_frames_per_step": n, "n_mel": n_mel, "d_model": d,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "conv stem step (row copies, conv0 and conv1 GEMMs on v_mfma_f32_32x32x16_bf16)",
+            "achieved": tfs,
+            "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s",
+            "frac": tfs / MFMA_BF16_PEAK_TFS,
+            "traffic": None,
+            "flops_per_step": flops,
+            "step_us_mean": t_step * 1e6,
+            "steps_timed": len(ms),
+        },
+    }
+
+
+def cpu_baseline_conv(steps: int):
+    """The fp64 oracle's streamed stem (oracle.conv.StreamStem), one stream,
+    `steps` feeds of 8 mel frames, one host thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import conv
+    from synth import conv_weights, mel_frames
+
+    w = conv_weights(6, 128, H * D)
+    mel = mel_frames(6, 0, 8 * steps, 128)
+    st = conv.StreamStem(w)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for i in range(steps):
+            st.feed(mel[8 * i:8 * i + 8])
+        el = time.perf_counter() - t0
+    return {"value": 4 * steps / el, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"one stream, {steps} feeds of 8 mel frames through oracle.conv.StreamStem "
+                      f"in fp64 numpy on one thread, {el:.1f} s"}
 
 
 KERNEL_SRC = os.path.join(ROOT, "sliding_window_cached_amd", "csrc", "vrt_kernels.hip")
@@ -812,7 +916,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2b", "c3", "c4", "copy"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2b", "c3", "c4", "cs", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ring", default="compact", choices=["compact", "mod"],
                     help="encoder configs: compacting ring (the pages') or modulo ring")
@@ -837,6 +941,10 @@ def main():
         args.steps = 300 if args.steps is None else args.steps
         args.warmup = 10 if args.warmup is None else args.warmup
         res = bench_c2b(args)
+    elif args.config == "cs":
+        args.steps = 300 if args.steps is None else args.steps
+        args.warmup = 10 if args.warmup is None else args.warmup
+        res = bench_cs(args)
     elif args.config == "c1":
         args.steps = 200 if args.steps is None else args.steps
         args.warmup = 10 if args.warmup is None else args.warmup
@@ -859,6 +967,8 @@ def main():
                                                "steady-state sample")
         elif args.config == "c2b":
             res["cpu_baseline"] = cpu_baseline_block(60)
+        elif args.config == "cs":
+            res["cpu_baseline"] = cpu_baseline_conv(40)
         elif args.config == "c1":
             res["cpu_baseline"] = cpu_baseline(1, 32, W, 400, 4, 0.5, [0], "staggered-streams sample")
         elif args.config == "c3":

@@ -290,6 +290,60 @@ vrt_status vrt_enc_block_feed(vrt_stream_state* const* states, int n_states, int
                               const void* x, int n_new, const vrt_block_weights* w, void* out,
                               void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---- The causal conv stem ahead of the encoder (family doc, "Architecture
+ * (summary)", Encoder bullet: n_mel -> d_model with kernel 3 and stride 1,
+ * then d_model -> d_model with kernel 3 and stride 2, each with bias and
+ * GELU; streaming-plan page, "Chunk alignment": left padding 2 and 1, kept
+ * across chunks as padding caches, so a streamed stem equals the offline
+ * one).  bf16 storage, fp32 accumulation on the matrix cores; the conv0
+ * output is rounded to bf16 where it is stored; GELU is the exact erf form.
+ *
+ * A stem object holds one stream's caches in caller-owned device memory: the
+ * last 2 mel frames, and the 1 or 2 conv0 frames that conv1's next stride-2
+ * window still needs.  Before the first feed both read as zeros (the causal
+ * padding); nothing is written at creation. */
+typedef struct vrt_conv_stem vrt_conv_stem;
+
+/* Device bytes of one stem (n_mel a multiple of 64, d_model of 128; 0 if
+ * not). */
+size_t vrt_conv_stem_device_bytes(int n_mel, int d_model);
+/* dev_mem: 256-byte aligned, at least vrt_conv_stem_device_bytes.
+ * VRT_ERR_UNSUPPORTED for other sizes, VRT_ERR_CAPACITY for short memory. */
+vrt_status vrt_conv_stem_create(int n_mel, int d_model, void* dev_mem, size_t bytes,
+                                vrt_conv_stem** out);
+/* Host-only: the caches read as zeros again, as before the first feed. */
+vrt_status vrt_conv_stem_reset(vrt_conv_stem* c);
+void vrt_conv_stem_destroy(vrt_conv_stem* c);
+/* Mel frames fed since the last reset, and conv0 frames pending (1 or 2). */
+vrt_status vrt_conv_stem_query(const vrt_conv_stem* c, int64_t* frames_in, int32_t* pending);
+/* Stem outputs a feed of n_frames mel frames would give: (pending + n - 1) / 2
+ * when pending + n >= 3, else 0 (8 frames after an 8-frame feed give 4).
+ * -1 on bad arguments.  Pure host planning. */
+int vrt_conv_out_frames(const vrt_conv_stem* c, int n_frames);
+
+/* Conv weights, device pointers, bf16, tap-major: w0[o][k * n_mel + c] is
+ * conv0's weight[o][c][k] (k = 0 the oldest frame), w1[o][k * d_model + c]
+ * conv1's; biases [d_model] or null. */
+typedef struct {
+    const void* w0;
+    const void* b0;
+    const void* w1;
+    const void* b1;
+} vrt_conv_weights;
+
+size_t vrt_conv_workspace_bytes(int n_mel, int d_model, int n_stems, int n_frames);
+
+/* Feed n_frames new mel frames to each of n_stems stems: mel
+ * [n_stems][n_frames][n_mel]; out [n_stems][*n_out][d_model] receives the
+ * stem outputs that became computable (*n_out = vrt_conv_out_frames).  All
+ * stems must have the same dimensions and the same pending count, and be
+ * distinct (VRT_ERR_INVALID otherwise); at most 256 per call.  mel, out,
+ * workspace, w0 and w1 16-byte aligned.  The caches advance as the work is
+ * enqueued. */
+vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const void* mel,
+                              int n_frames, const vrt_conv_weights* w, void* out, int32_t* n_out,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Per-component timing (the pages time each stage of a streamed feed on its
  * own: family doc, Capability Validation table, Streaming row, items 7 and
  * 8).  While both events are non-null, every later call on this thread

@@ -30,6 +30,9 @@ EXPORTS = (
     "vrt_offline_scratch_bytes", "vrt_enc_attn_offline", "vrt_enc_attn_feed",
     "vrt_ring_compact", "vrt_dec_workspace_bytes", "vrt_dec_attn_step", "vrt_set_attn_events",
     "vrt_rmsnorm", "vrt_linear", "vrt_block_workspace_bytes", "vrt_enc_block_feed",
+    "vrt_conv_stem_device_bytes", "vrt_conv_stem_create", "vrt_conv_stem_reset",
+    "vrt_conv_stem_destroy", "vrt_conv_stem_query", "vrt_conv_out_frames",
+    "vrt_conv_workspace_bytes", "vrt_conv_stem_feed",
 )
 
 
@@ -38,6 +41,12 @@ class BlockWeights(Structure):
     _fields_ = [("norm_w", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("b_q", ctypes.c_void_p),
                 ("b_v", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("b_o", ctypes.c_void_p),
                 ("eps", ctypes.c_float), ("reserved", c_int32)]
+
+
+class ConvWeights(Structure):
+    """vrt_conv_weights: tap-major conv weights and biases (device pointers)."""
+    _fields_ = [("w0", ctypes.c_void_p), ("b0", ctypes.c_void_p), ("w1", ctypes.c_void_p),
+                ("b1", ctypes.c_void_p)]
 
 
 class CacheDesc(Structure):
@@ -136,6 +145,15 @@ def _load():
         "vrt_block_workspace_bytes": (c_size_t, [POINTER(CacheDesc), c_int]),
         "vrt_enc_block_feed": (c_int, [POINTER(P), c_int, c_int, P, c_int, POINTER(BlockWeights), P,
                                        P, c_size_t, P]),
+        "vrt_conv_stem_device_bytes": (c_size_t, [c_int, c_int]),
+        "vrt_conv_stem_create": (c_int, [c_int, c_int, P, c_size_t, POINTER(P)]),
+        "vrt_conv_stem_reset": (c_int, [P]),
+        "vrt_conv_stem_destroy": (None, [P]),
+        "vrt_conv_stem_query": (c_int, [P, POINTER(c_int64), POINTER(c_int32)]),
+        "vrt_conv_out_frames": (c_int, [P, c_int]),
+        "vrt_conv_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+        "vrt_conv_stem_feed": (c_int, [POINTER(P), c_int, P, c_int, POINTER(ConvWeights), P,
+                                       POINTER(c_int32), P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -300,6 +318,66 @@ def enc_block_feed(states, layer, x, n_new, weights: BlockWeights, out, workspac
     if check:
         _check(s, "enc_block_feed")
     return s
+
+
+class ConvStem:
+    """One stream's conv stem caches over caller-owned device memory."""
+
+    def __init__(self, n_mel: int, d_model: int, dev_mem, nbytes: int):
+        self.mem = dev_mem          # keep the owner alive
+        h = c_void_p()
+        _check(lib.vrt_conv_stem_create(n_mel, d_model, _ptr(dev_mem), nbytes, byref(h)),
+               "conv_stem_create")
+        self.h = h
+
+    def reset(self):
+        _check(lib.vrt_conv_stem_reset(self.h), "conv_stem_reset")
+
+    def query(self):
+        f, p = c_int64(), c_int32()
+        _check(lib.vrt_conv_stem_query(self.h, byref(f), byref(p)), "conv_stem_query")
+        return f.value, p.value
+
+    def out_frames(self, n: int) -> int:
+        return lib.vrt_conv_out_frames(self.h, n)
+
+    def close(self):
+        if self.h:
+            lib.vrt_conv_stem_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def conv_stem_device_bytes(n_mel, d_model) -> int:
+    return lib.vrt_conv_stem_device_bytes(n_mel, d_model)
+
+
+def conv_workspace_bytes(n_mel, d_model, n_stems, n_frames) -> int:
+    return lib.vrt_conv_workspace_bytes(n_mel, d_model, n_stems, n_frames)
+
+
+def conv_weights(w0, b0, w1, b1) -> ConvWeights:
+    """Keep the owners alive while the struct is used."""
+    return ConvWeights(_ptr(w0), _ptr(b0), _ptr(w1), _ptr(b1))
+
+
+def conv_stem_feed(stems, mel, n_frames, weights: ConvWeights, out, workspace, ws_bytes, stream=0,
+                   check=True):
+    """Returns the number of stem outputs written per stem (or the status
+    when check is False and the call fails)."""
+    arr = (c_void_p * len(stems))(*[s.h for s in stems])
+    n_out = c_int32(0)
+    s = lib.vrt_conv_stem_feed(arr, len(stems), _ptr(mel), n_frames, byref(weights), _ptr(out),
+                               byref(n_out), _ptr(workspace), ws_bytes, stream)
+    if check:
+        _check(s, "conv_stem_feed")
+        return n_out.value
+    return s if s != OK else n_out.value
 
 
 def set_attn_events(start=None, stop=None):

@@ -129,17 +129,26 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     const char* A = (const char*)a.A;
     const char* W = (const char*)a.W;
 
+    // source row (tap 0) of each A row this lane fills: a fixed set of rows
+    long long arow[L::AIPW];
+#pragma unroll
+    for (int i = 0; i < L::AIPW; ++i) {
+        const int r = ((wave * L::AIPW + i) * 64 + lane) >> 3;
+        const int m = min(m0 + r, a.M - 1);
+        const int g = m / a.a_grp, li = m - g * a.a_grp;
+        arow[i] = (long long)g * a.a_gstride + (long long)li * a.a_stride;
+    }
     auto issue = [&](int kt, int st) {
         char* as = lds + st * L::STAGE;
         char* ws = as + L::ATILE;
         const long long kb = (long long)kt * L::BK * 2;
+        const int tap = (kt * L::BK) / a.a_cols, c0 = kt * L::BK - tap * a.a_cols;
 #pragma unroll
         for (int i = 0; i < L::AIPW; ++i) {
             const int ins = wave * L::AIPW + i;
             const int q = ins * 64 + lane;          // 16-byte chunk of the tile this lane fills
             const int r = q >> 3, c = (q & 7) ^ gsw(r);
-            const int ra = min(m0 + r, a.M - 1);
-            dma16(A + (long long)ra * a.lda * 2 + kb + 16 * c, as + ins * 1024);
+            dma16(A + ((arow[i] + tap) * a.lda + c0) * 2 + 16 * c, as + ins * 1024);
         }
 #pragma unroll
         for (int i = 0; i < L::WIPW; ++i) {
@@ -230,7 +239,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
                 if (a.R)
                     v += __uint_as_float(
                         (uint32_t)*(const uint16_t*)((const char*)a.R + ((long long)row * a.ldr + col) * 2) << 16);
-                *(uint16_t*)(out + ((long long)row * ldo + lc) * 2) = to_bf16(v);
+                if (a.act == 1) v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+                const int og = row / a.o_grp;
+                const long long orow = (long long)og * a.o_gstride + (row - og * a.o_grp) + a.o_off;
+                *(uint16_t*)(out + (orow * ldo + lc) * 2) = to_bf16(v);
             }
     }
 }
@@ -244,7 +256,34 @@ using G128 = GT<128, 128, 4>;
 using G64x128 = GT<64, 128, 3>;
 using G64 = GT<64, 64, 4>;
 
+// ------------------------------------------------------- conv stem rows ----
+// One workgroup per (stem, row): 16-byte chunks between a stem's cache rows
+// and its staging rows; a fresh stem's cache reads as zeros (the causal
+// left padding).
+__global__ __launch_bounds__(64) void k_row_copy(RowCopyArgs a, RowCopyTable t) {
+    const int g = blockIdx.x / a.rows, r = blockIdx.x - g * a.rows;
+    char* st = a.stage + ((long long)g * a.gstride + a.off + r) * a.row_bytes;
+    char* ca = (char*)t.cache[g] + (long long)r * a.row_bytes;
+    for (int c = threadIdx.x; c < a.row_bytes / 16; c += blockDim.x) {
+        if (a.to_cache) {
+            *(uint4*)(ca + 16 * c) = *(const uint4*)(st + 16 * c);
+        } else {
+            const uint4 v = (a.zero_from_cache && t.fresh[g]) ? make_uint4(0, 0, 0, 0)
+                                                             : *(const uint4*)(ca + 16 * c);
+            *(uint4*)(st + 16 * c) = v;
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s) {
+    if (a.n_groups < 1 || a.n_groups > kMaxStems || a.rows < 0 || a.row_bytes < 16 || a.row_bytes % 16)
+        return hipErrorInvalidValue;
+    if (a.rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_row_copy, dim3((unsigned)(a.n_groups * a.rows)), dim3(64), 0, s, a, t);
+    return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s) {
     if (a.rows < 1 || a.dim < 8 || a.dim % 8 != 0 || a.dim > 2048) return hipErrorInvalidValue;
@@ -254,7 +293,9 @@ hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.M < 1 || a.N < 128 || a.N % 128 != 0 || a.K < 64 || a.K % 64 != 0 || a.seg_w < 128 ||
-        a.seg_w % 128 != 0 || a.N != a.seg_w * a.n_seg || a.n_seg < 1 || a.n_seg > kMaxGemmSeg)
+        a.seg_w % 128 != 0 || a.N != a.seg_w * a.n_seg || a.n_seg < 1 || a.n_seg > kMaxGemmSeg ||
+        a.a_grp < 1 || a.a_stride < 0 || a.a_cols < 64 || a.a_cols % 64 != 0 || a.K % a.a_cols != 0 ||
+        a.a_gstride < 0 || a.o_grp < 1 || a.o_off < 0 || a.o_gstride < 0 || a.act < 0 || a.act > 1)
         return hipErrorInvalidValue;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||

@@ -692,6 +692,7 @@ vrt_status vrt_linear(const void* A, int M, int K, const void* W, int N, const v
     g.M = M;
     g.N = N;
     g.K = K;
+    gemm_plain(&g);
     g.seg_w = N;
     g.n_seg = 1;
     g.seg[0] = GemmSeg{out, bias, N};
@@ -746,6 +747,7 @@ vrt_status vrt_enc_block_feed(vrt_stream_state* const* st, int n_states, int lay
     g.M = M;
     g.N = 3 * dim;
     g.K = dim;
+    gemm_plain(&g);
     g.seg_w = dim;
     g.n_seg = 3;
     g.seg[0] = GemmSeg{q, w->b_q, dim};
@@ -764,10 +766,194 @@ vrt_status vrt_enc_block_feed(vrt_stream_state* const* st, int n_states, int lay
     o.M = M;
     o.N = dim;
     o.K = dim;
+    gemm_plain(&o);
     o.seg_w = dim;
     o.n_seg = 1;
     o.seg[0] = GemmSeg{out, w->b_o, dim};
     if (note(launch_gemm(o, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    return VRT_OK;
+}
+
+
+// ---- causal conv stem ahead of the encoder
+
+}  // extern "C"
+
+struct vrt_conv_stem {
+    int n_mel, d_model;
+    char* dev;          // mel cache [2][n_mel], then conv0 pending rows [2][d_model] (bf16)
+    size_t pend_off;
+    int pending;        // conv0 frames carried for conv1 (1 or 2)
+    bool fresh;         // caches hold nothing yet (they read as zeros)
+    int64_t frames_in;  // mel frames fed since the last reset
+};
+
+namespace {
+
+constexpr int kConvPad0 = 2;   // (kernel 3 - 1) + 1 - stride 1
+constexpr int kConvPad1 = 1;   // (kernel 3 - 1) + 1 - stride 2
+
+bool conv_dims_ok(int n_mel, int d_model) {
+    return n_mel >= 64 && n_mel % 64 == 0 && n_mel <= 4096 && d_model >= 128 && d_model % 128 == 0 &&
+           d_model <= 8192;
+}
+size_t pad256(size_t b) { return (b + 255) / 256 * 256; }
+// conv1 outputs of a feed whose staged conv0 rows number L (pending + new)
+int conv1_outputs(int L) { return L >= 3 ? (L - 1) / 2 : 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t vrt_conv_stem_device_bytes(int n_mel, int d_model) {
+    if (!conv_dims_ok(n_mel, d_model)) return 0;
+    return pad256((size_t)kConvPad0 * n_mel * 2) + pad256((size_t)2 * d_model * 2);
+}
+
+vrt_status vrt_conv_stem_create(int n_mel, int d_model, void* dev_mem, size_t bytes,
+                                vrt_conv_stem** out) {
+    if (!out || !dev_mem || ((uintptr_t)dev_mem & 255) != 0) return VRT_ERR_INVALID;
+    if (!conv_dims_ok(n_mel, d_model)) return VRT_ERR_UNSUPPORTED;
+    if (bytes < vrt_conv_stem_device_bytes(n_mel, d_model)) return VRT_ERR_CAPACITY;
+    vrt_conv_stem* c = new (std::nothrow) vrt_conv_stem;
+    if (!c) return VRT_ERR_CAPACITY;
+    c->n_mel = n_mel;
+    c->d_model = d_model;
+    c->dev = (char*)dev_mem;
+    c->pend_off = pad256((size_t)kConvPad0 * n_mel * 2);
+    c->pending = kConvPad1;
+    c->fresh = true;
+    c->frames_in = 0;
+    *out = c;
+    return VRT_OK;
+}
+
+vrt_status vrt_conv_stem_reset(vrt_conv_stem* c) {
+    if (!c) return VRT_ERR_INVALID;
+    c->pending = kConvPad1;
+    c->fresh = true;
+    c->frames_in = 0;
+    return VRT_OK;
+}
+
+void vrt_conv_stem_destroy(vrt_conv_stem* c) { delete c; }
+
+vrt_status vrt_conv_stem_query(const vrt_conv_stem* c, int64_t* frames_in, int32_t* pending) {
+    if (!c) return VRT_ERR_INVALID;
+    if (frames_in) *frames_in = c->frames_in;
+    if (pending) *pending = c->pending;
+    return VRT_OK;
+}
+
+int vrt_conv_out_frames(const vrt_conv_stem* c, int n_frames) {
+    if (!c || n_frames < 0) return -1;
+    return conv1_outputs(c->pending + n_frames);
+}
+
+size_t vrt_conv_workspace_bytes(int n_mel, int d_model, int n_stems, int n_frames) {
+    if (!conv_dims_ok(n_mel, d_model) || n_stems < 1 || n_frames < 1) return 0;
+    return pad256((size_t)n_stems * (n_frames + kConvPad0) * n_mel * 2) +
+           pad256((size_t)n_stems * (n_frames + 2) * d_model * 2);
+}
+
+vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const void* mel,
+                              int n_frames, const vrt_conv_weights* w, void* out, int32_t* n_out,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!stems || n_stems < 1 || n_stems > kMaxStems || !stems[0] || !mel || !w || !out || !n_out ||
+        !workspace || n_frames < 1)
+        return VRT_ERR_INVALID;
+    if (!w->w0 || !w->w1) return VRT_ERR_INVALID;
+    const int n_mel = stems[0]->n_mel, d = stems[0]->d_model, p = stems[0]->pending;
+    std::vector<const vrt_conv_stem*> seen;
+    for (int i = 0; i < n_stems; ++i) {
+        const vrt_conv_stem* c = stems[i];
+        if (!c || c->n_mel != n_mel || c->d_model != d || c->pending != p) return VRT_ERR_INVALID;
+        seen.push_back(c);
+    }
+    std::sort(seen.begin(), seen.end());
+    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return VRT_ERR_INVALID;
+    if ((long long)n_stems * (n_frames + kConvPad0) > INT_MAX / 2) return VRT_ERR_INVALID;
+    if (!aligned16(mel) || !aligned16(out) || !aligned16(workspace) || !aligned16(w->w0) ||
+        !aligned16(w->w1) || ((uintptr_t)w->b0 & 1) || ((uintptr_t)w->b1 & 1))
+        return VRT_ERR_INVALID;
+    if (ws_bytes < vrt_conv_workspace_bytes(n_mel, d, n_stems, n_frames)) return VRT_ERR_CAPACITY;
+
+    const int L = p + n_frames, o = conv1_outputs(L), keep = L - 2 * o;   // keep: 1 or 2
+    char* st0 = (char*)workspace;                       // [stem][n_frames + 2][n_mel]
+    char* st1 = st0 + pad256((size_t)n_stems * (n_frames + kConvPad0) * n_mel * 2);  // [stem][n_frames + 2][d]
+    RowCopyTable t0, t1;
+    for (int i = 0; i < n_stems; ++i) {
+        t0.cache[i] = (unsigned long long)(uintptr_t)stems[i]->dev;
+        t1.cache[i] = (unsigned long long)(uintptr_t)(stems[i]->dev + stems[i]->pend_off);
+        t0.fresh[i] = t1.fresh[i] = stems[i]->fresh ? 1 : 0;
+    }
+    clear_sticky_error();
+    auto copy = [&](const RowCopyTable& t, char* stage, long long gstride, long long off, int rows,
+                    int row_bytes, int to_cache) {
+        RowCopyArgs a{n_stems, rows, row_bytes, to_cache, stage, gstride, off, 1};
+        return note(launch_row_copy(a, t, stream));
+    };
+    // staging: [mel cache | new mel] and [pending conv0 rows | conv0 output]
+    if (copy(t0, st0, n_frames + kConvPad0, 0, kConvPad0, n_mel * 2, 0) != hipSuccess ||
+        copy(t1, st1, L, 0, p, d * 2, 0) != hipSuccess)
+        return VRT_ERR_DEVICE;
+    // the new mel rows go behind each stem's cache rows (one strided copy)
+    if (note(hipMemcpy2DAsync(st0 + (size_t)kConvPad0 * n_mel * 2, (size_t)(n_frames + kConvPad0) * n_mel * 2,
+                              mel, (size_t)n_frames * n_mel * 2, (size_t)n_frames * n_mel * 2, n_stems,
+                              hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+        return VRT_ERR_DEVICE;
+    GemmArgs g0{};
+    g0.A = st0;
+    g0.lda = n_mel;
+    g0.W = w->w0;
+    g0.ldw = 3 * n_mel;
+    g0.M = n_stems * n_frames;
+    g0.N = d;
+    g0.K = 3 * n_mel;
+    gemm_plain(&g0);
+    g0.a_grp = n_frames;
+    g0.a_gstride = n_frames + kConvPad0;
+    g0.a_stride = 1;
+    g0.a_cols = n_mel;
+    g0.o_grp = n_frames;
+    g0.o_gstride = L;
+    g0.o_off = p;
+    g0.act = 1;
+    g0.seg_w = d;
+    g0.n_seg = 1;
+    g0.seg[0] = GemmSeg{st1, w->b0, d};
+    if (note(launch_gemm(g0, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    if (o > 0) {
+        GemmArgs g1{};
+        g1.A = st1;
+        g1.lda = d;
+        g1.W = w->w1;
+        g1.ldw = 3 * d;
+        g1.M = n_stems * o;
+        g1.N = d;
+        g1.K = 3 * d;
+        gemm_plain(&g1);
+        g1.a_grp = o;
+        g1.a_gstride = L;
+        g1.a_stride = 2;
+        g1.a_cols = d;
+        g1.act = 1;
+        g1.seg_w = d;
+        g1.n_seg = 1;
+        g1.seg[0] = GemmSeg{out, w->b1, d};
+        if (note(launch_gemm(g1, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    }
+    // new caches: the last two staged mel rows; the conv0 rows from 2 o on
+    for (int i = 0; i < n_stems; ++i) t0.fresh[i] = t1.fresh[i] = 0;
+    if (copy(t0, st0, n_frames + kConvPad0, n_frames, kConvPad0, n_mel * 2, 1) != hipSuccess ||
+        copy(t1, st1, L, 2 * o, keep, d * 2, 1) != hipSuccess)
+        return VRT_ERR_DEVICE;
+    for (int i = 0; i < n_stems; ++i) {
+        stems[i]->pending = keep;
+        stems[i]->fresh = false;
+        stems[i]->frames_in += n_frames;
+    }
+    *n_out = o;
     return VRT_OK;
 }
 

@@ -124,16 +124,54 @@ struct GemmSeg {
     long long ld;
 };
 struct GemmArgs {
-    const void* A;      // [M][lda] bf16
+    const void* A;      // bf16 rows of lda elements (see the row addressing below)
     long long lda;
     const void* W;      // [N][ldw] bf16, one row per output column
     long long ldw;
-    const void* R;      // [M][ldr] bf16 residual added to every column, or null
+    const void* R;      // [M][ldr] bf16 residual (indexed by product row), or null
     long long ldr;
     int M, N, K;
     int seg_w, n_seg;
     GemmSeg seg[kMaxGemmSeg];
+    // A row addressing (an implicit im2col for convolutions): product row m
+    // of group g = m / a_grp, i = m % a_grp, reads for k in
+    // [t a_cols, (t + 1) a_cols) the source row g a_gstride + i a_stride + t.
+    // A plain product: a_grp = M, a_gstride = 0, a_stride = 1, a_cols = K.
+    int a_grp, a_stride, a_cols;
+    long long a_gstride;
+    // output rows: product row m is stored at row (m / o_grp) o_gstride +
+    // m % o_grp + o_off of its segment.  Plain: o_grp = M, o_gstride = 0, o_off = 0.
+    int o_grp, o_off;
+    long long o_gstride;
+    int act;            // 0: none; 1: GELU (exact, erf form) after bias and residual
 };
+inline void gemm_plain(GemmArgs* g) {
+    g->a_grp = g->M;
+    g->a_stride = 1;
+    g->a_cols = g->K;
+    g->a_gstride = 0;
+    g->o_grp = g->M;
+    g->o_off = 0;
+    g->o_gstride = 0;
+    g->act = 0;
+}
+
+// ---- causal conv stem (vrt_block.hip): row copies between each stem's
+// caches (device memory of its own, given by a table) and the staging rows
+constexpr int kMaxStems = 256;
+struct RowCopyArgs {
+    int n_groups, rows;         // copy `rows` rows for each of n_groups stems
+    int row_bytes;              // multiple of 16
+    int to_cache;               // 0: cache -> staging; 1: staging -> cache
+    char* stage;                // staging rows: group g row r at stage + (g gstride + off + r) row_bytes
+    long long gstride, off;
+    int zero_from_cache;        // cache -> staging: write zeros for groups marked fresh
+};
+struct RowCopyTable {
+    unsigned long long cache[kMaxStems];   // row 0 of each stem's cache rows
+    int fresh[kMaxStems];
+};
+hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s);
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);

@@ -98,6 +98,24 @@ def block_weights(seed: int, layer: int, dim: int, dtype: str = "bf16") -> dict:
     return w
 
 
+W0, B0, W1, B1 = range(20, 24)  # tensor ids of conv stem weights
+
+
+def conv_weights(seed: int, n_mel: int, d_model: int, dtype: str = "bf16") -> dict:
+    """Random conv stem weights in conv layout [out][in][kernel 3]: N(0, 1/fan_in)
+    matrices, 0.1 N(0,1) biases."""
+    s = 0x5EED2
+    return {"w0": normal(seed, s, 0, W0, (d_model, n_mel, 3), (3 * n_mel) ** -0.5, dtype),
+            "b0": normal(seed, s, 0, B0, (d_model,), 0.1, dtype),
+            "w1": normal(seed, s, 0, W1, (d_model, d_model, 3), (3 * d_model) ** -0.5, dtype),
+            "b1": normal(seed, s, 0, B1, (d_model,), 0.1, dtype)}
+
+
+def mel_frames(seed: int, stream: int, T: int, n_mel: int, dtype: str = "bf16") -> np.ndarray:
+    """Log-mel-like input rows [T][n_mel], N(0,1)."""
+    return normal(seed, stream, 0, X, (T, n_mel), 1.0, dtype)
+
+
 def offsets(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     """n integers uniform in [lo, hi) (start offsets, start positions or
     context lengths), from their own seed sequence."""

@@ -278,3 +278,30 @@ def test_block_entry_argument_checks():
     top = _state(d, 2 ** 31 - 3)
     assert vrt.enc_block_feed([top], 0, P, 4, bw, P, P, ws, check=False) == vrt.ERR_INVALID
     assert st.query(0) == (0, 0) and top.query(0) == (2 ** 31 - 3, 0)
+
+
+def test_conv_stem_host_rules():
+    """Host planning of the conv stem and argument errors before any enqueue."""
+    P = FAKE
+    nb = vrt.conv_stem_device_bytes(128, 1280)
+    assert nb == 512 + 5120
+    assert vrt.conv_stem_device_bytes(100, 1280) == 0
+    st = vrt.ConvStem(128, 1280, P, nb)
+    assert st.query() == (0, 1)
+    assert [st.out_frames(n) for n in (1, 2, 3, 8, 9)] == [0, 1, 1, 4, 4]
+    with pytest.raises(vrt.VrtError) as e:
+        vrt.ConvStem(128, 1280, P, nb - 1)
+    assert e.value.status == vrt.ERR_CAPACITY
+    with pytest.raises(vrt.VrtError) as e:
+        vrt.ConvStem(96, 1280, P, nb)
+    assert e.value.status == vrt.ERR_UNSUPPORTED
+    cw = vrt.conv_weights(P, P, P, P)
+    ws = vrt.conv_workspace_bytes(128, 1280, 2, 8)
+    other = vrt.ConvStem(128, 1280, P + (1 << 20), nb)
+    assert vrt.conv_stem_feed([st, st], P, 8, cw, P, P, ws, check=False) == vrt.ERR_INVALID
+    assert vrt.conv_stem_feed([st, other], P, 8, cw, P, P, ws - 1, check=False) == vrt.ERR_CAPACITY
+    assert vrt.conv_stem_feed([st], P, 0, cw, P, P, ws, check=False) == vrt.ERR_INVALID
+    assert vrt.conv_stem_feed([st], P + 8, 8, cw, P, P, ws, check=False) == vrt.ERR_INVALID
+    small = vrt.ConvStem(128, 256, P, vrt.conv_stem_device_bytes(128, 256))
+    assert vrt.conv_stem_feed([st, small], P, 8, cw, P, P, ws, check=False) == vrt.ERR_INVALID
+    assert st.query() == (0, 1)
