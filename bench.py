@@ -22,6 +22,7 @@ c2b           the c2 step through the attention half of an encoder block
 c4            decoder step: 32 streams x 26 layers, GQA 32/8 x 128, window 8192.
 cs            the causal conv stem: 256 streams x 8 mel frames per step.
 copy          calibration copy of 1 GiB for the HBM byte counters.
+read          calibration: a plain streaming read of 4 GiB (the practical ceiling).
 
 --ring mod runs c1, c2 or c3 with the encoder cache kept as a modulo ring
 (1280 slots, slot = position % slots, no compaction; outputs bit-identical
@@ -579,6 +580,31 @@ def bench_copy(args):
             "steps": args.steps}
 
 
+def bench_read(args):
+    """Calibration: the library's read probe streams 4 GiB (16-byte loads,
+    eight in flight per thread); the practical ceiling of a read-bound
+    kernel on the part, beside the nominal 8 TB/s."""
+    import torch
+    import sliding_window_cached_amd as vrt
+    n = 1 << 32
+    x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        vrt.read_probe(x, n, sink, stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        vrt.read_probe(x, n, sink, stream)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / args.steps
+    return {"metric": "device streaming read bandwidth (calibration)", "value": n / t / 1e9,
+            "unit": "GB/s", "frac_of_nominal": n / t / 1e9 / HBM_PEAK_GBS, "bytes_read_per_launch": n,
+            "steps": args.steps, "kernel": "k_read_probe (vrt_read_probe)"}
+
+
 def bench_c1(args):
     """64 streams x 32 independent layer caches, bf16 N(0,1)*0.5.  Stream i
     first ingests o_i ~ U{0..749} frames (one untimed catch-up feed) so ring
@@ -916,7 +942,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2b", "c3", "c4", "cs", "copy"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2b", "c3", "c4", "cs", "copy", "read"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ring", default="compact", choices=["compact", "mod"],
                     help="encoder configs: compacting ring (the pages') or modulo ring")
@@ -932,6 +958,11 @@ def main():
         args.steps = 20 if args.steps is None else args.steps
         args.warmup = 2 if args.warmup is None else args.warmup
         print(json.dumps(bench_copy(args)), flush=True)
+        return
+    if args.config == "read":
+        args.steps = 20 if args.steps is None else args.steps
+        args.warmup = 2 if args.warmup is None else args.warmup
+        print(json.dumps(bench_read(args)), flush=True)
         return
     if args.config == "c2":
         args.steps = 1000 if args.steps is None else args.steps

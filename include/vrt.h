@@ -344,6 +344,13 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
                               int n_frames, const vrt_conv_weights* w, void* out, int32_t* n_out,
                               void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Measurement only: one pass that reads bytes / 16 16-byte chunks of buf
+ * (16-byte aligned) as fast as the part allows and writes nothing but,
+ * never in practice, one word to sink (4-byte aligned).  Timing it gives the
+ * practical streaming-read ceiling beside the nominal HBM bandwidth (the
+ * survey's advice: confirm the constants with measured kernels). */
+vrt_status vrt_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);
+
 /* Per-component timing (the pages time each stage of a streamed feed on its
  * own: family doc, Capability Validation table, Streaming row, items 7 and
  * 8).  While both events are non-null, every later call on this thread

@@ -32,7 +32,7 @@ EXPORTS = (
     "vrt_rmsnorm", "vrt_linear", "vrt_block_workspace_bytes", "vrt_enc_block_feed",
     "vrt_conv_stem_device_bytes", "vrt_conv_stem_create", "vrt_conv_stem_reset",
     "vrt_conv_stem_destroy", "vrt_conv_stem_query", "vrt_conv_out_frames",
-    "vrt_conv_workspace_bytes", "vrt_conv_stem_feed",
+    "vrt_conv_workspace_bytes", "vrt_conv_stem_feed", "vrt_read_probe",
 )
 
 
@@ -152,6 +152,7 @@ def _load():
         "vrt_conv_stem_query": (c_int, [P, POINTER(c_int64), POINTER(c_int32)]),
         "vrt_conv_out_frames": (c_int, [P, c_int]),
         "vrt_conv_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+        "vrt_read_probe": (c_int, [P, c_size_t, P, P]),
         "vrt_conv_stem_feed": (c_int, [POINTER(P), c_int, P, c_int, POINTER(ConvWeights), P,
                                        POINTER(c_int32), P, c_size_t, P]),
     }
@@ -378,6 +379,10 @@ def conv_stem_feed(stems, mel, n_frames, weights: ConvWeights, out, workspace, w
         _check(s, "conv_stem_feed")
         return n_out.value
     return s if s != OK else n_out.value
+
+
+def read_probe(buf, nbytes, sink, stream=0):
+    _check(lib.vrt_read_probe(_ptr(buf), nbytes, _ptr(sink), stream), "read_probe")
 
 
 def set_attn_events(start=None, stop=None):

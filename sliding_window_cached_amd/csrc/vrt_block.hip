@@ -275,7 +275,42 @@ __global__ __launch_bounds__(64) void k_row_copy(RowCopyArgs a, RowCopyTable t) 
     }
 }
 
+// ------------------------------------------------ read-ceiling probe ----
+// Measurement only: every thread streams 16-byte chunks of a buffer (eight
+// loads in flight per round, grid-stride) and folds them with XOR; the fold
+// is stored only when it equals a value the caller never passes, so the
+// loads cannot be removed.  Its rate is the practical ceiling of a
+// read-bound kernel on the part, beside the nominal HBM figure.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, long long n16,
+                                                    unsigned magic, unsigned* sink) {
+    constexpr int U = 8;
+    const long long stride = (long long)gridDim.x * blockDim.x * U;
+    uint4 acc = make_uint4(0, 0, 0, 0);
+    for (long long i = (long long)blockIdx.x * blockDim.x * U + threadIdx.x; i < n16; i += stride) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long j = i + (long long)u * blockDim.x;
+            v[u] = j < n16 ? p[j] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            acc.x ^= v[u].x;
+            acc.y ^= v[u].y;
+            acc.z ^= v[u].z;
+            acc.w ^= v[u].w;
+        }
+    }
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == magic) sink[0] = 1u;
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, hipStream_t s) {
+    hipLaunchKernelGGL(k_read_probe, dim3(16384), dim3(256), 0, s, (const uint4*)buf,
+                       (long long)(bytes / 16), 0x9e3779b9u, sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s) {
     if (a.n_groups < 1 || a.n_groups > kMaxStems || a.rows < 0 || a.row_bytes < 16 || a.row_bytes % 16)

@@ -129,17 +129,23 @@ float scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)
 
 
 // kv heads per attention workgroup: the largest divisor of hkv whose rotated
-// query rows fit the workgroup's LDS budget and that still leaves about four
-// workgroups per compute unit, so each workgroup streams a long run of tiles
-// through one pipeline.
+// query rows fit the workgroup's LDS budget and that still leaves a full
+// round of workgroups (as many per CU as the kernel's LDS allows, at most 4),
+// so each workgroup streams a long run of tiles through one pipeline.
 int pick_hg(const Geom& g, long long units, int rows_per_head, long long qchunks, long long splits) {
-    int dev = 0, cus = 0;
+    int dev = 0, cus = 0, lds = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    const long long target = 4LL * cus;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        lds <= 0)
+        lds = 160 * 1024;
     const int elem = g.dtype == 1 ? 2 : 4;
+    const long long wg_lds = (long long)attn_stages(g.dtype, g.D, splits > 1) * 2 * kTile * g.D * elem +
+                             kQsBytes + 4 * kTile * elem;
+    const long long per_cu = std::max(1LL, std::min(4LL, lds / wg_lds));
+    const long long target = per_cu * cus;
     int best = 1;
     for (int h = 2; h <= g.hkv; ++h) {
         if (g.hkv % h) continue;
@@ -955,6 +961,12 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
     }
     *n_out = o;
     return VRT_OK;
+}
+
+vrt_status vrt_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream) {
+    if (!buf || !sink || bytes < 16 || !aligned16(buf) || ((uintptr_t)sink & 3)) return VRT_ERR_INVALID;
+    clear_sticky_error();
+    return note(launch_read_probe(buf, bytes, (unsigned*)sink, stream)) == hipSuccess ? VRT_OK : VRT_ERR_DEVICE;
 }
 
 }  // extern "C"

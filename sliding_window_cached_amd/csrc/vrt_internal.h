@@ -32,6 +32,15 @@ constexpr int kSplitLen = 1024;
 // exp2(SENT - SENT) = 1 keeps fully masked tiles exact no-ops).
 constexpr float kSent = -1.0e30f;
 
+// LDS tile stages of the vector-path attention kernel per (storage dtype,
+// head_dim, split mode); the host sizes its workgroups-per-CU target by it.
+// Two everywhere: three or four stages (fewer workgroups per CU, more bytes
+// in flight per CU) measured the same on the serving and decoder workloads,
+// which already stream near the part's read ceiling.
+constexpr int attn_stages(int dtype, int D, bool split) {
+    return 2 + 0 * (dtype + D + (split ? 1 : 0));
+}
+
 // Geometry of one cache kind, shared by every state of a launch.
 struct Geom {
     int dtype;          // 0 f32, 1 bf16
@@ -172,6 +181,7 @@ struct RowCopyTable {
     int fresh[kMaxStems];
 };
 hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);

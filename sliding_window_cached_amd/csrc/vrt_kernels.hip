@@ -337,12 +337,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 // workgroups whose key range ends at the newest frame (chunk 0; in split mode
 // the last split) also rotate and write the new K/V rows of their kv heads
 // before any tile holding them is read.
-template <class E, int D>
+template <class E, int D, int NST_>
 struct Tl {
     static constexpr int RB = D * E::E;          // bytes per K / V row
     static constexpr int CPR = RB / 16;          // 16-byte chunks per row
     static constexpr int TILE = kTile * RB;      // bytes of one K (or V) tile
-    static constexpr int NST = 2;                // LDS stages (tiles); T+1 streams while T is read
+    static constexpr int NST = NST_;             // LDS stages (tiles); NST - 1 stream while one is read
     static constexpr int IPW = CPR / 4;          // DMA instructions per wave per K (or V) tile
     static constexpr int LPW = 2 * IPW;          // DMA instructions per wave per tile
     static constexpr int PRB = kTile * E::E;     // bytes of one P row
@@ -397,7 +397,7 @@ __device__ __forceinline__ void wait_vm() {
 // row of the current head is kept in registers for that head's key loop).
 template <class E, int D, bool MOD, bool SPLIT, bool APPEND, int RPW>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
-    using L = Tl<E, D>;
+    using L = Tl<E, D, attn_stages(E::E == 2 ? 1 : 0, D, SPLIT)>;
     constexpr int H2 = D / 2, CG = H2 / 4, DPL = D / 64;
     __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
     char* Qs = lds + L::NST * 2 * L::TILE;
@@ -542,13 +542,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     const int x0i = threadIdx.x;
     if (x0i < items) load_item(x0i, first);
 
-    // Tiles without new rows may be fetched before the append: both stages are
-    // free at the start, so up to two tiles go out ahead of the prologue.
+    // Tiles without new rows may be fetched before the append: every stage is
+    // free at the start, so up to NST tiles go out ahead of the prologue (the
+    // rest of the first NST follow the prologue's barrier; tiles with new rows
+    // are the last ones of a head, so the ones held back always follow the
+    // ones issued, and tiles go out in order).
     constexpr int PRE = L::NST;
     bool pre_done[PRE];
+    bool held = false;
 #pragma unroll
     for (int st = 0; st < PRE; ++st) {
-        pre_done[st] = st < ntt && !has_new(st);
+        held = held || !(st < ntt && !has_new(st));
+        pre_done[st] = !held;
         if (pre_done[st]) issue(st, st);
     }
 
@@ -594,15 +599,27 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
                 for (int c = 0; c < L::CPR; ++c) qreg[c] = *(const uint4*)(qr + 16 * c);
             }
         }
-        // Outstanding here: tile T, plus tile 1 when T = 0 (tiles 0 and 1 were
-        // both issued, in that order, before the loop).  Tile T+1 (T >= 1) goes
-        // out only after the barrier frees its stage.
-        if (T == 0 && ntt > 1)
-            wait_vm<L::LPW>();
-        else
-            wait_vm<0>();
+        // Outstanding here: tile T and the tiles issued after it, in order:
+        // tiles 1 .. NST-1 when T = 0 (the first NST went out before the
+        // loop), else tiles T+1 .. T+NST-2 (tile T+NST-1 goes out only after
+        // the barrier frees its stage).
+        {
+            const int after = T == 0 ? min(L::NST - 1, ntt - 1) : min(L::NST - 2, ntt - 1 - T);
+            if constexpr (L::NST >= 4) {
+                if (after >= 3) wait_vm<3 * L::LPW>();
+                else if (after == 2) wait_vm<2 * L::LPW>();
+                else if (after == 1) wait_vm<L::LPW>();
+                else wait_vm<0>();
+            } else if constexpr (L::NST == 3) {
+                if (after >= 2) wait_vm<2 * L::LPW>();
+                else if (after == 1) wait_vm<L::LPW>();
+                else wait_vm<0>();
+            } else {
+                if (after >= 1) wait_vm<L::LPW>(); else wait_vm<0>();
+            }
+        }
         __syncthreads();   // every wave's share of T landed; T-1's stage is free
-        if (T >= 1 && T + 1 < ntt) issue(T + 1, (T + 1) % L::NST);
+        if (T >= 1 && T + L::NST - 1 < ntt) issue(T + L::NST - 1, (T + L::NST - 1) % L::NST);
         const char* Ks = lds + (T % L::NST) * 2 * L::TILE;
         const char* Vs = Ks + L::TILE;
         const int tb = it * kTile;   // tile start relative to tile 0

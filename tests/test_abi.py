@@ -305,3 +305,11 @@ def test_conv_stem_host_rules():
     small = vrt.ConvStem(128, 256, P, vrt.conv_stem_device_bytes(128, 256))
     assert vrt.conv_stem_feed([st, small], P, 8, cw, P, P, ws, check=False) == vrt.ERR_INVALID
     assert st.query() == (0, 1)
+
+
+def test_read_probe_argument_checks():
+    P = FAKE
+    assert vrt.lib.vrt_read_probe(None, 1 << 20, P, None) == vrt.ERR_INVALID
+    assert vrt.lib.vrt_read_probe(P + 8, 1 << 20, P, None) == vrt.ERR_INVALID
+    assert vrt.lib.vrt_read_probe(P, 8, P, None) == vrt.ERR_INVALID
+    assert vrt.lib.vrt_read_probe(P, 1 << 20, None, None) == vrt.ERR_INVALID
