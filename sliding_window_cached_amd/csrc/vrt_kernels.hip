@@ -1107,14 +1107,17 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
                                                      false, false);
     const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     if (jq >= nqw) return;
+    // one reciprocal per query instead of 32 divisions (the outputs are
+    // rounded to bf16 right after)
+    const float rl = 1.0f / l;
     char* dst = (char*)a.out + ((cu * m.n_total + frame) * a.g.hq + g) * (long long)(L::D * 2);
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             uint2 v;
-            v.x = pack_bf16x2(o[d][4 * q4] / l, o[d][4 * q4 + 1] / l);
-            v.y = pack_bf16x2(o[d][4 * q4 + 2] / l, o[d][4 * q4 + 3] / l);
+            v.x = pack_bf16x2(o[d][4 * q4] * rl, o[d][4 * q4 + 1] * rl);
+            v.y = pack_bf16x2(o[d][4 * q4 + 2] * rl, o[d][4 * q4 + 3] * rl);
             gst<uint2>(dst + 2 * (32 * d + 8 * q4 + 4 * hf), v);
         }
 }
