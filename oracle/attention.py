@@ -108,3 +108,34 @@ def windowed_at(q, k, v, start_pos: int, window: int, theta: float, ts) -> np.nd
         qr = rope.apply(np.asarray(q[t:t + 1], dtype=np.float64), pos[-1:], theta)[0]
         out.append(window_rows(qr, kr, np.asarray(v[u0:t + 1], dtype=np.float64), group))
     return np.stack(out)
+
+
+def lookahead(q, k, v, left: int, right: int) -> np.ndarray:
+    """Sliding-window attention with right lookahead and no rotation, over a
+    whole sequence (moonshine forward map, "Per-layer sliding-window mask" and
+    the streaming encoder's "Encoder attention" note: no RoPE, per-layer
+    (left, right) windows).  The query at t sees the keys u with
+    t - u in [0, left) or u - t in (0, right): positions t-left+1 .. t+right-1
+    clipped to the sequence.  q [T][Hq][d], k and v [T][Hkv][d]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hq, d = q.shape
+    group = Hq // k.shape[1]
+    out = np.empty((T, Hq, d), dtype=np.float64)
+    for t in range(T):
+        u0 = max(0, t - left + 1)
+        u1 = min(T - 1, t + max(right - 1, 0))
+        out[t] = window_rows(q[t], k[u0:u1 + 1], v[u0:u1 + 1], group)
+    return out
+
+
+def lookahead_mask(T: int, left: int, right: int) -> np.ndarray:
+    """The page's mask as a T x T boolean matrix, written out entry by entry:
+    visible[q][k] = (q - k in [0, left)) or (k - q in (0, right))."""
+    m = np.zeros((T, T), dtype=bool)
+    for a in range(T):
+        for b in range(T):
+            m[a, b] = (0 <= a - b < left) or (0 < b - a < right)
+    return m
+

@@ -117,3 +117,36 @@ def test_sampled_rows_equal_whole_sequence():
     ts = [0, 1, 6, 7, 30, 49]
     part = attention.windowed_at(q, k, v, 300, W, THETA, ts)
     assert np.array_equal(part, full[ts])
+
+
+# ---- (left, right) lookahead windows without rotation (moonshine pattern)
+
+def _masked_sdpa(q, k, v, mask):
+    """float64 torch SDPA with an explicit boolean mask (True = visible)."""
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))
+    kt = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))
+    vt = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask))
+    return o.numpy().transpose(1, 0, 2)
+
+
+@pytest.mark.parametrize("T,left,right", [(20, 16, 4), (20, 16, 0), (9, 3, 2), (12, 1, 1), (7, 30, 30)])
+def test_lookahead_against_masked_sdpa(T, left, right):
+    q, k, v = _rand(T + left + right, T, 2, 2, 8)
+    mask = attention.lookahead_mask(T, left, right)
+    got = attention.lookahead(q, k, v, left, right)
+    ref = _masked_sdpa(q, k, v, mask)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_lookahead_special_cases():
+    q, k, v = _rand(5, 10, 2, 2, 4)
+    assert np.array_equal(attention.lookahead(q, k, v, 1, 0), v)          # self only
+    assert np.array_equal(attention.lookahead(q, k, v, 1, 1), v)          # right = 1: no future
+    full = attention.lookahead(q, k, v, 100, 100)                         # whole sequence
+    ref = _masked_sdpa(q, k, v, np.ones((10, 10), dtype=bool))
+    assert np.max(np.abs(full - ref)) <= 1e-12
+    # the page's (16, 4): frame 5 sees frames 0 .. 8
+    m = attention.lookahead_mask(20, 16, 4)
+    assert list(np.nonzero(m[5])[0]) == list(range(0, 9))
+    assert list(np.nonzero(m[19])[0]) == list(range(4, 20))
