@@ -21,6 +21,7 @@ c2b           the c2 step through the attention half of an encoder block
               (RMSNorm, q/k/v projection, the path, output projection).
 c4            decoder step: 32 streams x 26 layers, GQA 32/8 x 128, window 8192.
 cs            the causal conv stem: 256 streams x 8 mel frames per step.
+cm            six (left, right)-window layers without RoPE (the moonshine pattern).
 copy          calibration copy of 1 GiB for the HBM byte counters.
 read          calibration: a plain streaming read of 4 GiB (the practical ceiling).
 
@@ -501,6 +502,123 @@ def bench_cs(args):
     }
 
 
+def bench_cm(args):
+    """The moonshine streaming encoder's attention pattern on the same
+    kernels: 256 streams, 4 new frames per stream per step through six layers
+    with (left, right) windows (16,4),(16,4),(16,0),(16,0),(16,4),(16,4), no
+    rotation; 8 heads of 64 (the pages' tiny model has heads of 40, which
+    these kernels do not take), bf16 N(0,1)*0.5."""
+    import torch
+    import sliding_window_cached_amd as vrt
+
+    dev = torch.device("cuda:0")
+    S, n, Hm, Dm = 256, 4, 8, 64
+    groups = [(vrt.lookahead_desc(16, 4, n_layers=4, heads=Hm, head_dim=Dm), 4),
+              (vrt.lookahead_desc(16, 0, n_layers=2, heads=Hm, head_dim=Dm), 2)]
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    total = args.warmup + args.steps
+    pools = []
+    for desc, L in groups:
+        nb = vrt.state_device_bytes(desc)
+        mem = torch.empty(S * nb, dtype=torch.uint8, device=dev)
+        states = [vrt.StreamState(desc, mem[i * nb:(i + 1) * nb], nb, 0) for i in range(S)]
+        qkv = [_randn(gen, (total, S, L, n, Hm, Dm), 0.5, dev) for _ in range(3)]
+        pools.append((desc, L, mem, states, qkv, torch.empty((S, L, n, Hm, Dm), dtype=torch.bfloat16, device=dev)))
+
+    def step(i):
+        for desc, L, _, states, (Q, K, V), out in pools:
+            vrt.enc_attn_feed(states, 0, L, Q[i], K[i], V[i], n, out, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    every = max(1, args.timing_every)
+    timed = list(range(0, args.steps, every))
+    ev = dict(zip(timed, _timing_events(len(timed))))
+    log(f"cm: timing {args.steps} steps of 6 lookahead layers")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        if j in ev:
+            ev[j][0].record()
+        step(args.warmup + j)
+        if j in ev:
+            ev[j][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[j][0].elapsed_time(ev[j][1]) for j in timed]
+    for p in pools:
+        for st in p[3]:
+            st.close()
+    row = Hm * Dm * 2
+    # per (stream, layer): q, k, v read, K/V appended, the keys of the union
+    # window read (15 + F + n rows of K and V), outputs written
+    nbytes = sum(S * L * (n + 2 * n + 2 * n + 2 * (15 + max(d.lookahead - 1, 0) + n) + n) * row
+                 for d, L, *_ in pools)
+    t_step = sum(ms) * 1e-3 / len(ms)
+    gbs = nbytes / t_step / 1e9
+    return {
+        "metric": "encoder frames/s through six (left, right)-window attention layers (all streams)",
+        "value": S * n * args.steps / wall,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "moonshine-pattern attention: 256 streams, 4 frames per step, 6 layers with "
+                        "(left, right) windows (16,4),(16,4),(16,0),(16,0),(16,4),(16,4), no RoPE, "
+                        "8 heads x 64, bf16 N(0,1)*0.5; answered frames lag by 3 in the (16,4) layers",
+            "streams": S, "layers": 6, "frames_per_step": n, "heads": Hm, "head_dim": Dm,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_attn lookahead path + append + waiting-row save (two feed calls per step)",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "alg_bytes_per_step": nbytes,
+            "step_us_mean": t_step * 1e6,
+            "steps_timed": len(ms),
+            "note": "windows of at most 23 keys: launch- and latency-bound, not bandwidth-bound",
+        },
+    }
+
+
+def cpu_baseline_cm(steps: int):
+    """The fp64 oracle (oracle.attention.lookahead over the frames seen so
+    far, the answered rows only) for one stream through one (16,4) layer, 4
+    frames per feed; scaled to the six layers of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention
+    from synth import qkv
+
+    T = 16 + 4 * steps + 3
+    q, k, v = qkv(7, 0, 0, T, 8, 8, 64, 0.5, "bf16")
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for i in range(steps):          # a feed of 4 frames answers 4 queries, 3 frames back
+            for t in range(16 + 4 * i, 16 + 4 * i + 4):
+                attention.window_rows(q[t], k[t - 15:t + 4], v[t - 15:t + 4], 1)
+        el = time.perf_counter() - t0
+    return {"value": 4 * steps / el / 6, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"one stream, one (16,4) layer, {steps} feeds of 4 frames; each answered query "
+                      f"over its window (oracle.attention.window_rows, fp64 numpy, one thread), "
+                      f"{el:.1f} s; divided by 6 layers"}
+
+
 def cpu_baseline_conv(steps: int):
     """The fp64 oracle's streamed stem (oracle.conv.StreamStem), one stream,
     `steps` feeds of 8 mel frames, one host thread."""
@@ -942,7 +1060,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c2b", "c3", "c4", "cs", "copy", "read"])
+    ap.add_argument("--config", default="c2",
+                    choices=["c1", "c2", "c2b", "c3", "c4", "cs", "cm", "copy", "read"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ring", default="compact", choices=["compact", "mod"],
                     help="encoder configs: compacting ring (the pages') or modulo ring")
@@ -976,6 +1095,10 @@ def main():
         args.steps = 300 if args.steps is None else args.steps
         args.warmup = 10 if args.warmup is None else args.warmup
         res = bench_cs(args)
+    elif args.config == "cm":
+        args.steps = 300 if args.steps is None else args.steps
+        args.warmup = 10 if args.warmup is None else args.warmup
+        res = bench_cm(args)
     elif args.config == "c1":
         args.steps = 200 if args.steps is None else args.steps
         args.warmup = 10 if args.warmup is None else args.warmup
@@ -1000,6 +1123,8 @@ def main():
             res["cpu_baseline"] = cpu_baseline_block(60)
         elif args.config == "cs":
             res["cpu_baseline"] = cpu_baseline_conv(40)
+        elif args.config == "cm":
+            res["cpu_baseline"] = cpu_baseline_cm(10000)
         elif args.config == "c1":
             res["cpu_baseline"] = cpu_baseline(1, 32, W, 400, 4, 0.5, [0], "staggered-streams sample")
         elif args.config == "c3":

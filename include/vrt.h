@@ -68,7 +68,8 @@ typedef enum { VRT_F32 = 0, VRT_BF16 = 1 } vrt_dtype;
 typedef enum {
     VRT_ENC_RING = 0,     /* encoder: contiguous ring + compaction */
     VRT_DEC_MODRING = 1,  /* decoder: slot = position % ring_slots */
-    VRT_ENC_MODRING = 2   /* encoder: slot = position % ring_slots, no compaction */
+    VRT_ENC_MODRING = 2,  /* encoder: slot = position % ring_slots, no compaction */
+    VRT_ENC_LOOKAHEAD = 3 /* encoder with (left, right) windows and no RoPE, modulo ring */
 } vrt_cache_kind;
 
 /* Everything about a cache is fixed when its states are created
@@ -84,7 +85,15 @@ typedef enum {
  * pages validate their decoder ring the same way, by an A/B against a buffer
  * that never wraps).  It needs ring_slots >= window - 1 + max_batch (a
  * sub-batch never overwrites a row one of its own queries reads), a multiple
- * of 64 (a 64-key tile never wraps); 1280 for the encoder above. */
+ * of 64 (a 64-key tile never wraps); 1280 for the encoder above.
+ * ENC_LOOKAHEAD is the moonshine streaming encoder's attention (moonshine
+ * forward map, "Per-layer sliding-window mask" and "Encoder attention": no
+ * RoPE, per-layer (left, right) windows): a query at t sees the keys u with
+ * t - u in [0, window) or u - t in (0, lookahead), so lookahead - 1 future
+ * frames.  A query is answered once its last future frame has been fed; the
+ * queries still waiting keep their q rows in the state.  rope_theta must be
+ * 0; ring_slots >= window + F + max_batch - 1 (F = future frames), a
+ * multiple of 64.  Layers with different windows use different descs. */
 typedef struct {
     int32_t kind;        /* vrt_cache_kind */
     int32_t dtype;       /* vrt_dtype: storage and I/O type; accumulation is fp32 */
@@ -97,7 +106,7 @@ typedef struct {
                             multiple of 64; ENC_MODRING: >= window - 1 + max_batch,
                             multiple of 64 */
     int32_t max_batch;   /* encoder kinds: largest sub-batch per append (feeds are split) */
-    int32_t reserved;    /* must be 0 */
+    int32_t lookahead;   /* ENC_LOOKAHEAD: the right bound R above; 0 for every other kind */
     double rope_theta;   /* NEOX RoPE base; omega_i = theta^(-2i/head_dim) */
 } vrt_cache_desc;
 
@@ -114,17 +123,21 @@ const char* vrt_version(void);
 const char* vrt_last_device_error(void);
 
 /* Check a descriptor without creating anything.  VRT_ERR_INVALID for
- * non-positive sizes or a reserved field != 0; VRT_ERR_UNSUPPORTED for a
+ * non-positive sizes, a nonzero lookahead outside ENC_LOOKAHEAD, or a
+ * nonzero rope_theta inside it; VRT_ERR_UNSUPPORTED for a
  * head_dim other than 64/128, an unknown dtype/kind, an ENC_RING ring smaller
  * than window + max_batch (streaming-plan page, "Unbounded length": batches
  * of at most 512 frames so one feed can never overflow the 1536-slot ring),
- * a decoder ring smaller than the window or not a multiple of 64, or an
+ * a decoder ring smaller than the window or not a multiple of 64, an
  * ENC_MODRING ring smaller than window - 1 + max_batch or not a multiple
- * of 64. */
+ * of 64, or an ENC_LOOKAHEAD ring smaller than window + F + max_batch - 1 or
+ * not a multiple of 64. */
 vrt_status vrt_desc_check(const vrt_cache_desc* desc);
 
 /* Device bytes one state needs: for each layer a K ring and a V ring, each
- * [n_heads_kv][ring_slots][head_dim] elements.  0 if the desc is invalid. */
+ * [n_heads_kv][ring_slots][head_dim] elements; for ENC_LOOKAHEAD then, per
+ * layer, F rows of n_heads_q * head_dim elements of waiting queries.  0 if
+ * the desc is invalid. */
 size_t vrt_state_device_bytes(const vrt_cache_desc* desc);
 
 /* Byte offset, inside a state's device memory, of row 0 of the ring slice
@@ -180,6 +193,12 @@ vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32
  * agree within bf16 rounding. */
 int vrt_attn_path(const vrt_cache_desc* desc, int n);
 
+/* Outputs a feed of n_new frames produces per (state, layer) when that layer
+ * has been fed n_kv frames before: n_new for ENC_RING and ENC_MODRING;
+ * max(0, n_kv + n_new - F) - max(0, n_kv - F) for ENC_LOOKAHEAD (a query is
+ * answered once F frames past it exist).  -1 for invalid arguments. */
+int vrt_attn_out_frames(const vrt_cache_desc* desc, int32_t n_kv, int n_new);
+
 /* Offline windowed attention over one whole sequence (streaming-plan page,
  * "Why offline == streaming" and the bounded-window re-encode section: the
  * whole-clip encoder under the 750-frame windowed-causal mask).
@@ -203,6 +222,9 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
  * also sees the earlier new frames of its feed).
  * q/out: [n_states][n_layers][n_new][n_heads_q][head_dim];
  * k/v:   [n_states][n_layers][n_new][n_heads_kv][head_dim].
+ * For ENC_LOOKAHEAD the answered queries are written, oldest first, to the
+ * first vrt_attn_out_frames rows of each (state, layer) in out; every
+ * (state, layer) of the call must hold the same number of waiting queries.
  * All states must share one desc (field-wise equal) and be distinct.
  * VRT_ERR_INVALID on null pointers, n_new < 1, bad layer range, mixed descs,
  * a repeated state, or a decoder state. */

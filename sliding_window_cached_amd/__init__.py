@@ -20,13 +20,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvrt.so")
 
 F32, BF16 = 0, 1
-ENC_RING, DEC_MODRING, ENC_MODRING = 0, 1, 2
+ENC_RING, DEC_MODRING, ENC_MODRING, ENC_LOOKAHEAD = 0, 1, 2, 3
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE, ERR_POISONED = range(6)
 
 EXPORTS = (
     "vrt_status_str", "vrt_version", "vrt_last_device_error", "vrt_desc_check", "vrt_state_device_bytes",
     "vrt_ring_offset", "vrt_stream_state_create", "vrt_stream_state_reset",
     "vrt_stream_state_destroy", "vrt_stream_state_query", "vrt_ring_advance", "vrt_attn_path",
+    "vrt_attn_out_frames",
     "vrt_offline_scratch_bytes", "vrt_enc_attn_offline", "vrt_enc_attn_feed",
     "vrt_ring_compact", "vrt_dec_workspace_bytes", "vrt_dec_attn_step", "vrt_set_attn_events",
     "vrt_rmsnorm", "vrt_linear", "vrt_block_workspace_bytes", "vrt_enc_block_feed",
@@ -54,7 +55,7 @@ class CacheDesc(Structure):
         ("kind", c_int32), ("dtype", c_int32), ("n_layers", c_int32),
         ("n_heads_q", c_int32), ("n_heads_kv", c_int32), ("head_dim", c_int32),
         ("window", c_int32), ("ring_slots", c_int32), ("max_batch", c_int32),
-        ("reserved", c_int32), ("rope_theta", c_double),
+        ("lookahead", c_int32), ("rope_theta", c_double),
     ]
 
 
@@ -68,6 +69,17 @@ def enc_desc(dtype=BF16, n_layers=1, heads=20, head_dim=64, window=750, ring_slo
         ring_slots = 1536 if kind == ENC_RING else -(-(window - 1 + max_batch) // 64) * 64
     return CacheDesc(kind, dtype, n_layers, heads, heads, head_dim, window, ring_slots,
                      max_batch, 0, theta)
+
+
+def lookahead_desc(left, right, dtype=BF16, n_layers=1, heads=8, head_dim=64, max_batch=512,
+                   ring_slots=None) -> CacheDesc:
+    """(left, right) windows without RoPE (the moonshine streaming encoder's
+    per-layer masks): keys u with t - u in [0, left) or u - t in (0, right)."""
+    f = max(right - 1, 0)
+    if ring_slots is None:
+        ring_slots = -(-(left + f + max_batch - 1) // 64) * 64
+    return CacheDesc(ENC_LOOKAHEAD, dtype, n_layers, heads, heads, head_dim, left, ring_slots,
+                     max_batch, right, 0.0)
 
 
 def dec_desc(dtype=BF16, n_layers=1, heads_q=32, heads_kv=8, head_dim=128, window=8192,
@@ -131,6 +143,7 @@ def _load():
         "vrt_ring_advance": (c_int, [POINTER(CacheDesc), POINTER(c_int64), POINTER(c_int32), c_int,
                                      POINTER(c_int32)]),
         "vrt_attn_path": (c_int, [POINTER(CacheDesc), c_int]),
+        "vrt_attn_out_frames": (c_int, [POINTER(CacheDesc), c_int32, c_int]),
         "vrt_offline_scratch_bytes": (c_size_t, [POINTER(CacheDesc), c_int]),
         "vrt_enc_attn_offline": (c_int, [POINTER(CacheDesc), P, P, P, c_int, c_int64, P, P,
                                          c_size_t, P]),
@@ -201,6 +214,10 @@ def state_device_bytes(desc: CacheDesc) -> int:
 
 def ring_offset(desc: CacheDesc, layer: int, which: int, kv_head: int) -> int:
     return lib.vrt_ring_offset(byref(desc), layer, which, kv_head)
+
+
+def attn_out_frames(desc: CacheDesc, n_kv: int, n_new: int) -> int:
+    return lib.vrt_attn_out_frames(byref(desc), n_kv, n_new)
 
 
 def attn_path(desc: CacheDesc, n: int) -> int:

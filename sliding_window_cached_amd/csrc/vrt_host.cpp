@@ -63,6 +63,7 @@ int elem_bytes(const vrt_cache_desc& d) { return d.dtype == VRT_BF16 ? 2 : 4; }
 
 bool same_desc(const vrt_cache_desc& a, const vrt_cache_desc& b) {
     return a.kind == b.kind && a.dtype == b.dtype && a.n_layers == b.n_layers &&
+           a.lookahead == b.lookahead &&
            a.n_heads_q == b.n_heads_q && a.n_heads_kv == b.n_heads_kv &&
            a.head_dim == b.head_dim && a.window == b.window && a.ring_slots == b.ring_slots &&
            a.max_batch == b.max_batch && a.rope_theta == b.rope_theta;
@@ -70,15 +71,18 @@ bool same_desc(const vrt_cache_desc& a, const vrt_cache_desc& b) {
 
 vrt_status check_desc(const vrt_cache_desc* d) {
     if (!d) return VRT_ERR_INVALID;
-    if (d->reserved != 0) return VRT_ERR_INVALID;
-    if (d->kind != VRT_ENC_RING && d->kind != VRT_DEC_MODRING && d->kind != VRT_ENC_MODRING)
+    if (d->kind != VRT_ENC_RING && d->kind != VRT_DEC_MODRING && d->kind != VRT_ENC_MODRING &&
+        d->kind != VRT_ENC_LOOKAHEAD)
         return VRT_ERR_UNSUPPORTED;
+    const bool look = d->kind == VRT_ENC_LOOKAHEAD;
+    if (look ? (d->lookahead < 0 || d->lookahead > (1 << 16)) : d->lookahead != 0) return VRT_ERR_INVALID;
     if (d->dtype != VRT_F32 && d->dtype != VRT_BF16) return VRT_ERR_UNSUPPORTED;
     if (d->n_layers < 1 || d->n_heads_q < 1 || d->n_heads_kv < 1 || d->window < 1 ||
         d->ring_slots < 1 || d->max_batch < 1)
         return VRT_ERR_INVALID;
     if (d->n_heads_q % d->n_heads_kv != 0) return VRT_ERR_INVALID;
-    if (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta)) return VRT_ERR_INVALID;
+    if (look ? d->rope_theta != 0.0 : (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta)))
+        return VRT_ERR_INVALID;
     if (d->head_dim != 64 && d->head_dim != 128) return VRT_ERR_UNSUPPORTED;
     const int group = d->n_heads_q / d->n_heads_kv;
     if (group > kRows) return VRT_ERR_UNSUPPORTED;
@@ -86,6 +90,13 @@ vrt_status check_desc(const vrt_cache_desc* d) {
         return VRT_ERR_UNSUPPORTED;
     if (d->kind == VRT_ENC_RING) {
         if ((int64_t)d->ring_slots < (int64_t)d->window + d->max_batch) return VRT_ERR_UNSUPPORTED;
+    } else if (look) {
+        // the oldest key a sub-batch's first answered query reads lies
+        // window - 1 + F frames before the sub-batch's newest frame
+        const int64_t f = std::max(d->lookahead - 1, 0);
+        if ((int64_t)d->ring_slots < (int64_t)d->window + f + d->max_batch - 1 ||
+            d->ring_slots % kTile != 0)
+            return VRT_ERR_UNSUPPORTED;
     } else if (d->kind == VRT_ENC_MODRING) {
         // a sub-batch of max_batch frames, written before its attention, must
         // not overwrite the oldest key (window - 1 back) its first query reads
@@ -99,7 +110,14 @@ vrt_status check_desc(const vrt_cache_desc* d) {
 }
 
 bool is_encoder(const vrt_cache_desc& d) {
-    return d.kind == VRT_ENC_RING || d.kind == VRT_ENC_MODRING;
+    return d.kind == VRT_ENC_RING || d.kind == VRT_ENC_MODRING || d.kind == VRT_ENC_LOOKAHEAD;
+}
+// future frames a query of a lookahead cache waits for (0 for other kinds)
+int look_f(const vrt_cache_desc& d) {
+    return d.kind == VRT_ENC_LOOKAHEAD ? std::max(d.lookahead - 1, 0) : 0;
+}
+size_t pend_layer_bytes(const vrt_cache_desc& d) {
+    return (size_t)look_f(d) * d.n_heads_q * d.head_dim * (d.dtype == VRT_BF16 ? 2 : 4);
 }
 
 size_t slice_bytes(const vrt_cache_desc& d) {
@@ -117,11 +135,12 @@ Geom make_geom(const vrt_cache_desc& d) {
     g.slots = d.ring_slots;
     g.window = d.window;
     g.mod = d.kind == VRT_ENC_RING ? 0 : 1;
+    g.rope = d.kind == VRT_ENC_LOOKAHEAD ? 0 : 1;
     g.slice_bytes = (long long)slice_bytes(d);
     g.v_off = (long long)d.n_heads_kv * g.slice_bytes;
     g.layer_bytes = 2 * g.v_off;
     for (int i = 0; i < 64; ++i)
-        g.omega[i] = i < d.head_dim / 2 ? std::pow(d.rope_theta, -2.0 * i / d.head_dim) : 0.0;
+        g.omega[i] = (g.rope && i < d.head_dim / 2) ? std::pow(d.rope_theta, -2.0 * i / d.head_dim) : 0.0;
     return g;
 }
 
@@ -160,7 +179,7 @@ int pick_hg(const Geom& g, long long units, int rows_per_head, long long qchunks
 // description and n, so two feeds that split a sequence differently but take
 // the same path produce bit-identical outputs.
 bool use_mfma(const vrt_cache_desc& d, int n) {
-    return is_encoder(d) && d.dtype == VRT_BF16 && d.head_dim == 64 &&
+    return is_encoder(d) && d.kind != VRT_ENC_LOOKAHEAD && d.dtype == VRT_BF16 && d.head_dim == 64 &&
            d.n_heads_q == d.n_heads_kv && n >= kMfmaMinFrames;
 }
 
@@ -344,7 +363,7 @@ vrt_status vrt_desc_check(const vrt_cache_desc* desc) { return check_desc(desc);
 
 size_t vrt_state_device_bytes(const vrt_cache_desc* desc) {
     if (check_desc(desc) != VRT_OK) return 0;
-    return (size_t)desc->n_layers * layer_bytes(*desc);
+    return (size_t)desc->n_layers * (layer_bytes(*desc) + pend_layer_bytes(*desc));
 }
 
 size_t vrt_ring_offset(const vrt_cache_desc* desc, int layer, int which, int kv_head) {
@@ -397,7 +416,7 @@ vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32
     const vrt_status s = check_desc(desc);
     if (s != VRT_OK) return s;
     if (!is_encoder(*desc) || !abs_base || !n_kv || n_new < 0) return VRT_ERR_INVALID;
-    if (desc->kind == VRT_ENC_MODRING) {   // every frame is kept: n_kv counts them all
+    if (desc->kind != VRT_ENC_RING) {   // modulo rings: n_kv counts every frame
         if (*n_kv < 0 || *abs_base < 0 || *abs_base + *n_kv > kPosLimit - n_new)
             return VRT_ERR_INVALID;
         *n_kv += n_new;
@@ -419,6 +438,12 @@ vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32
     *n_kv = nkv;
     if (n_compactions) *n_compactions = nc;
     return VRT_OK;
+}
+
+int vrt_attn_out_frames(const vrt_cache_desc* desc, int32_t n_kv, int n_new) {
+    if (check_desc(desc) != VRT_OK || !is_encoder(*desc) || n_kv < 0 || n_new < 0) return -1;
+    const int f = look_f(*desc);
+    return (int)(std::max<int64_t>(0, (int64_t)n_kv + n_new - f) - std::max<int64_t>(0, (int64_t)n_kv - f));
 }
 
 int vrt_attn_path(const vrt_cache_desc* desc, int n) {
@@ -467,7 +492,7 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
     clear_sticky_error();
     if (note(launch_rope_append(aa, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
 
-    AttnArgs at;
+    AttnArgs at{};
     at.g = g;
     at.m = m;
     at.q = q;
@@ -477,6 +502,8 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
     const bool mfma = use_mfma(*desc, T);
     attn_shape(g, mfma, 1, T, &at);
     at.append = 0;   // the append above already wrote every row
+    at.look_f = look_f(*desc);   // lookahead: every frame answered, the last ones see the end
+    at.look_nout = T;
     if (note(launch_attn(at, mfma, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
     return VRT_OK;
 }
@@ -494,9 +521,17 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
 
     const vrt_cache_desc& d = st[0]->d;
     const Geom g = make_geom(d);
+    // lookahead: every (state, layer) of the call holds the same number of
+    // waiting queries, so one launch answers the same count for all
+    const int F = look_f(d);
+    const int wait0 = (int)std::min<int64_t>(st[0]->n_kv[layer0], F);
+    for (int i = 0; i < n_states; ++i)
+        for (int l = layer0; l < layer0 + n_layers; ++l)
+            if (std::min<int64_t>(st[i]->n_kv[l], F) != wait0) return VRT_ERR_INVALID;
     clear_sticky_error();
-    int t0 = 0;
+    int t0 = 0, o_written = 0;
     for (int m : split_feed(n_new, d.max_batch)) {
+        int n_out_sb = m;
         std::vector<std::pair<int, int>> comp;
         if (d.kind == VRT_ENC_RING)
             for (int i = 0; i < n_states; ++i)
@@ -515,13 +550,43 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
             aa.m = um;
             aa.k = k;
             aa.v = v;
-            AttnArgs at;
+            AttnArgs at{};
             at.g = g;
             at.m = um;
             at.q = q;
             at.k = k;
             at.v = v;
             at.out = out;
+            if (d.kind == VRT_ENC_LOOKAHEAD) {
+                // append (no rotation), answer the queries whose last future
+                // frame now exists, keep the rest waiting
+                const int pw = (int)std::min<int64_t>(st[p.states[0]]->n_kv[layer0 + p.l_off], F);
+                n_out_sb = pw == F ? m : std::max(0, pw + m - F);
+                const int keep = pw == F ? F : std::min(pw + m, F);
+                at.look_f = F;
+                at.look_pend = pw;
+                at.look_nout = n_out_sb;
+                at.look_o0 = o_written;
+                at.pend_off = (long long)d.n_layers * (long long)layer_bytes(d);
+                at.pend_layer = (long long)pend_layer_bytes(d);
+                at.partials = nullptr;
+                at.n_splits = 1;
+                at.split_len = kSplitLen;
+                at.scale_log2 = scale_log2(g.D);
+                at.append = 0;
+                at.qchunk = kRows / g.group;
+                at.n_qchunks = (n_out_sb + at.qchunk - 1) / at.qchunk;
+                at.hg = n_out_sb > 0 ? pick_hg(g, (long long)um.n_states * um.nl,
+                                               std::min(at.qchunk, n_out_sb) * g.group, at.n_qchunks, 1)
+                                     : 1;
+                if (note(launch_rope_append(aa, t, stream)) != hipSuccess ||
+                    (n_out_sb > 0 && note(launch_attn(at, false, t, stream)) != hipSuccess) ||
+                    note(launch_pend_save(at, t, keep, stream)) != hipSuccess) {
+                    poison(st, n_states);
+                    return VRT_ERR_DEVICE;
+                }
+                continue;
+            }
             const bool mfma = use_mfma(d, m);
             attn_shape(g, mfma, (long long)um.n_states * um.nl, m, &at);
             if ((!at.append && note(launch_rope_append(aa, t, stream)) != hipSuccess) ||
@@ -533,6 +598,7 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
         for (int i = 0; i < n_states; ++i)
             for (int l = layer0; l < layer0 + n_layers; ++l) st[i]->n_kv[l] += m;
         t0 += m;
+        o_written += n_out_sb;
     }
     return VRT_OK;
 }
@@ -608,7 +674,7 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int laye
             aa.m = um;
             aa.k = k;
             aa.v = v;
-            AttnArgs at;
+            AttnArgs at{};
             at.g = g;
             at.m = um;
             at.q = q;

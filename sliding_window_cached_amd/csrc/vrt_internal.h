@@ -49,6 +49,7 @@ struct Geom {
     int slots;          // ring slots per (layer, kv head)
     int window;         // W
     int mod;            // 1: slot = pos % slots; 0: slot = pos - abs_base
+    int rope;           // 1: q and k are rotated at their positions; 0: no rotation
     long long layer_bytes;  // bytes per layer inside a state (K ring + V ring)
     long long slice_bytes;  // bytes per kv-head slice = slots * D * elem
     long long v_off;        // byte offset of the V ring inside a layer
@@ -102,7 +103,20 @@ struct AttnArgs {
     float scale_log2;   // log2(e) / sqrt(D)
     int append;         // 1: the attention launch also appends the new K/V rows
     int hg;             // kv heads per workgroup (divides hkv)
+    // (left, right) windows: query i of this launch (0 <= i < look_nout) sits
+    // at p0 - look_pend + i, sees keys up to look_f frames past itself (up to
+    // the newest frame written), and takes its q row from the state's waiting
+    // rows when i < look_pend, else from new frame i - look_pend; its output
+    // goes to row look_o0 + i of the call's output
+    int look_f, look_pend, look_nout, look_o0;
+    long long pend_off;       // byte offset, in a state, of layer 0's waiting q rows
+    long long pend_layer;     // bytes of one layer's waiting rows (look_f rows)
 };
+
+// Waiting q rows after a sub-batch of a lookahead cache: the last `keep`
+// rows of [the `pend` waiting rows | the sub-batch's q rows] (a forward copy
+// in place: every row moves to a lower or equal index)
+hipError_t launch_pend_save(const AttnArgs& a, const StateTable& t, int keep, hipStream_t s);
 
 struct CompactTable {
     unsigned long long layer_ring[kMaxCompact];  // base of the (state, layer) K ring

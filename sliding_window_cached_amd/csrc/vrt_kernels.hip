@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
     const int f0 = fb * FR, nf = min(FR, m.n - f0);
     for (int x = threadIdx.x; x < nf * H2; x += blockDim.x) {
         const int f = x / H2, i = x - f * H2;
-        cs[x] = rope_of<E>(p0 + f0 + f, a.g.omega[i]);
+        if (a.g.rope) cs[x] = rope_of<E>(p0 + f0 + f, a.g.omega[i]);
     }
     __syncthreads();
     const int hkv = a.g.hkv;
@@ -230,9 +230,15 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
         float x0[4], x1[4], y0[4], y1[4];
         ld4<E>(src + 4 * c * E::E, x0);
         ld4<E>(src + (H2 + 4 * c) * E::E, x1);
+        if (a.g.rope) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            rope_pair(x0[q], x1[q], cs[f * H2 + 4 * c + q], &y0[q], &y1[q]);
+            for (int q = 0; q < 4; ++q) rope_pair(x0[q], x1[q], cs[f * H2 + 4 * c + q], &y0[q], &y1[q]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                y0[q] = x0[q];
+                y1[q] = x1[q];
+            }
         }
         char* dst = layer + (long long)h * a.g.slice_bytes + slot * (D * E::E);
         st4<E, true>(dst + 4 * c * E::E, y0);
@@ -395,7 +401,11 @@ __device__ __forceinline__ void wait_vm() {
 
 // RPW: rows per wave (1 when a head has at most 4 rows; then the wave's query
 // row of the current head is kept in registers for that head's key loop).
-template <class E, int D, bool MOD, bool SPLIT, bool APPEND, int RPW>
+// LOOK: (left, right) windows without rotation (moonshine streaming encoder):
+// the launch answers look_nout queries that lag the newest frame, each seeing
+// look_f frames past itself; the oldest look_pend of them come from the q rows
+// the state keeps waiting.
+template <class E, int D, bool MOD, bool SPLIT, bool APPEND, int RPW, bool LOOK>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     using L = Tl<E, D, attn_stages(E::E == 2 ? 1 : 0, D, SPLIT)>;
     constexpr int H2 = D / 2, CG = H2 / 4, DPL = D / 64;
@@ -433,11 +443,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
 
     const int W = a.g.window, group = a.g.group;
     const long long avail = t.p0[si] - t.n_kv[si];             // abs_base / first position
-    const long long pq0 = t.p0[si] + (long long)qc * a.qchunk;  // first query of the chunk
-    const int nq = min(a.qchunk, m.n - qc * a.qchunk);
+    const int npend = LOOK ? a.look_pend : 0;                   // queries answered from waiting rows
+    const long long pq0 = t.p0[si] - npend + (long long)qc * a.qchunk;  // first query of the chunk
+    const int nq = min(a.qchunk, (LOOK ? a.look_nout : m.n) - qc * a.qchunk);
     const int R = nq * group;                                   // rows per head
+    const int fut = LOOK ? a.look_f : 0;                        // frames a query sees past itself
     long long wlo = max(avail, pq0 - W + 1);
     long long whi = pq0 + nq - 1;
+    if (LOOK) whi = min(t.p0[si] + m.n - 1, whi + fut);         // up to the newest frame written
     bool appender = APPEND && qc == 0;
     if (SPLIT) {
         const long long s_abs = floor_div(wlo, a.split_len) + split;
@@ -496,9 +509,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         const int c = x % CG, r = (x / CG) % R, hh = x / (CG * R);
         const int j = r / group, gh = r - j * group;
         const int g = g0 + hh;
-        const long long frame = m.t0 + (long long)qc * a.qchunk + j;
-        const char* src = (const char*)a.q +
-                          ((cu * m.n_total + frame) * qrow + (long long)(g * group + gh) * D) * E::E;
+        const int qi = qc * a.qchunk + j;                       // query index in the launch
+        const long long frame = m.t0 + (long long)qi - npend;   // its new frame (qi >= npend)
+        const char* src;
+        if (LOOK && qi < npend)   // a waiting q row of this (state, layer)
+            src = (const char*)t.ring[si] + a.pend_off + (long long)(m.layer0 + m.l_off + li) * a.pend_layer +
+                  ((long long)qi * qrow + (long long)(g * group + gh) * D) * E::E;
+        else
+            src = (const char*)a.q + ((cu * m.n_total + frame) * qrow + (long long)(g * group + gh) * D) * E::E;
         ld4<E>(src + 4 * c * E::E, it.x0);
         ld4<E>(src + (H2 + 4 * c) * E::E, it.x1);
         if (APPEND && appender && gh == 0) {
@@ -517,10 +535,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         const long long pos = pq0 + j;
         Angle<E> an[4];
         float y0[4], y1[4];
+        if constexpr (LOOK) {   // no rotation
 #pragma unroll
-        for (int q = 0; q < 4; ++q) an[q] = rope_of<E>(pos, a.g.omega[4 * c + q]);
+            for (int q = 0; q < 4; ++q) {
+                y0[q] = it.x0[q];
+                y1[q] = it.x1[q];
+            }
+        } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rope_pair(it.x0[q], it.x1[q], an[q], &y0[q], &y1[q]);
+            for (int q = 0; q < 4; ++q) an[q] = rope_of<E>(pos, a.g.omega[4 * c + q]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rope_pair(it.x0[q], it.x1[q], an[q], &y0[q], &y1[q]);
+        }
         char* dst = Qs + (hh * R + r) * L::RB;
         st4<E, false>(dst + 4 * c * E::E, y0);
         st4<E, false>(dst + (H2 + 4 * c) * E::E, y1);
@@ -579,7 +605,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     for (int i = 0; i < RPW; ++i) {
         const long long pq = pq0 + (wave + 4 * i) / group;
         rlo[i] = (int)(max(wlo, pq - W + 1) - T0);
-        rhi[i] = (int)(min(whi, pq) - T0);
+        rhi[i] = (int)(min(whi, pq + fut) - T0);
     }
     uint4 qreg[RPW == 1 ? L::CPR : 1];
 
@@ -724,9 +750,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
                     for (int k = 0; k < DPL; ++k) gst<float>(pr + 2 + lane + 64 * k, acc[i][k]);
                 } else {
                     const int hq = g * group + gh;
-                    char* dst = (char*)a.out +
-                                ((cu * m.n_total + m.t0 + (long long)qc * a.qchunk + j) * a.g.hq + hq) *
-                                    (long long)D * E::E;
+                    const long long orow = (LOOK ? (long long)a.look_o0 : (long long)m.t0) + (long long)qc * a.qchunk + j;
+                    char* dst = (char*)a.out + ((cu * m.n_total + orow) * a.g.hq + hq) * (long long)D * E::E;
 #pragma unroll
                     for (int k = 0; k < DPL; ++k) {
                         const float o = acc[i][k] / lrow;
@@ -1122,6 +1147,33 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
         }
 }
 
+// ------------------------------------------ waiting rows (lookahead) ----
+// One thread per 16-byte column of a q row: the last `keep` rows of [the
+// waiting rows | this sub-batch's q rows] move to the front of the waiting
+// rows.  Source index >= destination index for every row, and a thread
+// copies its column's rows in ascending order, so the copy is safe in place.
+template <class E, int D>
+__global__ __launch_bounds__(64) void k_pend_save(AttnArgs a, StateTable t, int keep) {
+    const UnitMap& m = a.m;
+    const long long row = (long long)a.g.hq * D * E::E;
+    const int nch = (int)(row / 16), bpu = (nch + 63) / 64;
+    const int unit = blockIdx.x / bpu, c = (blockIdx.x - unit * bpu) * 64 + threadIdx.x;
+    if (c >= nch) return;
+    const int si = unit / m.nl, li = unit - si * m.nl;
+    const long long cu = (long long)t.call_idx[si] * m.nl_call + m.l_off + li;
+    char* pend = (char*)t.ring[si] + a.pend_off + (long long)(m.layer0 + m.l_off + li) * a.pend_layer;
+    const int p = a.look_pend, shift = p + m.n - keep;
+    for (int r = 0; r < keep; ++r) {
+        const int src = shift + r;
+        uint4 v;
+        if (src < p)
+            v = gld<uint4>(pend + src * row + 16 * c);
+        else
+            v = gld<uint4>((const char*)a.q + (cu * m.n_total + m.t0 + (src - p)) * row + 16 * c);
+        gst<uint4>(pend + r * row + 16 * c, v);
+    }
+}
+
 // ---------------------------------------------- K5b: split-K merge ----
 // One wave per (unit, q head), lane = output dim.  Splits are merged in
 // ascending absolute order; splits past the window were never written.
@@ -1195,16 +1247,27 @@ hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t 
     const dim3 grid((unsigned)blocks), block(256);
     const bool split = a.n_splits > 1 || a.partials != nullptr;
     const bool app = a.append != 0;
-    const bool one = (long long)std::min(a.qchunk, a.m.n) * a.g.group <= 4;  // <= 1 row per wave
+    const int nqs = a.g.rope ? a.m.n : a.look_nout;   // queries per unit in this launch
+    const bool one = (long long)std::min(a.qchunk, nqs) * a.g.group <= 4;  // <= 1 row per wave
 #define VRT_ATTN(MOD, SPLIT, APP)                                                                   \
     do {                                                                                            \
         if (one)                                                                                    \
-            hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, 1>), grid, block, 0, s, a, t);      \
+            hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, 1, false>), grid, block, 0, s, a, t); \
         else                                                                                        \
-            hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, kRows / 4>), grid, block, 0, s, a, t); \
+            hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, kRows / 4, false>), grid, block, 0, s, a, t); \
     } while (0)
+#define VRT_LOOK(MOD)                                                                               \
+    do {                                                                                            \
+        if (one)                                                                                    \
+            hipLaunchKernelGGL((k_attn<E_, D_, MOD, false, false, 1, true>), grid, block, 0, s, a, t); \
+        else                                                                                        \
+            hipLaunchKernelGGL((k_attn<E_, D_, MOD, false, false, kRows / 4, true>), grid, block, 0, s, a, t); \
+    } while (0)
+    if (!a.g.rope && (split || app)) return hipErrorInvalidValue;
     VRT_DISPATCH_ED(a.g.dtype, a.g.D, {
-        if (a.g.mod && split && app) VRT_ATTN(true, true, true);
+        if (!a.g.rope && a.g.mod) VRT_LOOK(true);
+        else if (!a.g.rope) VRT_LOOK(false);
+        else if (a.g.mod && split && app) VRT_ATTN(true, true, true);
         else if (a.g.mod && split) VRT_ATTN(true, true, false);
         else if (a.g.mod && app) VRT_ATTN(true, false, true);
         else if (a.g.mod) VRT_ATTN(true, false, false);
@@ -1212,6 +1275,7 @@ hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t 
         else VRT_ATTN(false, false, false);
     });
 #undef VRT_ATTN
+#undef VRT_LOOK
     return hipGetLastError();
 }
 
@@ -1220,6 +1284,17 @@ hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t 
         return hipErrorInvalidValue;
     const long long blocks = (long long)a.m.n_states * a.m.nl * a.g.hkv * a.n_qchunks;
     hipLaunchKernelGGL(k_attn_mfma, dim3((unsigned)blocks), dim3(256), 0, s, a, t);
+    return hipGetLastError();
+}
+
+hipError_t launch_pend_save(const AttnArgs& a, const StateTable& t, int keep, hipStream_t s) {
+    if (keep < 1) return hipSuccess;
+    const long long row = (long long)a.g.hq * a.g.D * (a.g.dtype == 1 ? 2 : 4);
+    const long long bpu = (row / 16 + 63) / 64;
+    const dim3 grid((unsigned)((long long)a.m.n_states * a.m.nl * bpu));
+    VRT_DISPATCH_ED(a.g.dtype, a.g.D, {
+        hipLaunchKernelGGL((k_pend_save<E_, D_>), grid, dim3(64), 0, s, a, t, keep);
+    });
     return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ def test_desc_checks():
     assert vrt.desc_check(vrt.dec_desc(ring_slots=8200)) == vrt.ERR_UNSUPPORTED  # not 64-multiple
     assert vrt.desc_check(vrt.dec_desc(ring_slots=16384)) == vrt.OK
     d = vrt.enc_desc()
-    d.reserved = 1
+    d.lookahead = 1                      # only for ENC_LOOKAHEAD
     assert vrt.desc_check(d) == vrt.ERR_INVALID
     assert vrt.desc_check(vrt.enc_desc(heads=0)) == vrt.ERR_INVALID
     assert vrt.desc_check(vrt.dec_desc(heads_q=30)) == vrt.ERR_INVALID  # not a multiple of 8
@@ -90,7 +90,7 @@ def test_attn_path_is_a_function_of_desc_and_n():
         assert vrt.attn_path(vrt.enc_desc(head_dim=128), n) == 0
     assert vrt.attn_path(bf, 0) == -1
     bad = vrt.enc_desc()
-    bad.reserved = 3
+    bad.lookahead = 3
     assert vrt.attn_path(bad, 64) == -1
 
 
@@ -313,3 +313,32 @@ def test_read_probe_argument_checks():
     assert vrt.lib.vrt_read_probe(P + 8, 1 << 20, P, None) == vrt.ERR_INVALID
     assert vrt.lib.vrt_read_probe(P, 8, P, None) == vrt.ERR_INVALID
     assert vrt.lib.vrt_read_probe(P, 1 << 20, None, None) == vrt.ERR_INVALID
+
+
+def test_lookahead_host_rules():
+    """ENC_LOOKAHEAD descs: no rotation (rope_theta 0), the ring must hold
+    window + F + max_batch - 1 rows (F = lookahead - 1 future frames), a
+    multiple of 64; answered-query counts; the vector path only; waiting
+    q rows in the state; states with different numbers of waiting queries
+    never share a call."""
+    d = vrt.lookahead_desc(16, 4)
+    assert d.ring_slots == 576 and vrt.desc_check(d) == vrt.OK          # 16 + 3 + 512 - 1 = 530
+    bad = vrt.lookahead_desc(16, 4)
+    bad.rope_theta = 1.0e6
+    assert vrt.desc_check(bad) == vrt.ERR_INVALID
+    assert vrt.desc_check(vrt.lookahead_desc(16, 4, ring_slots=512)) == vrt.ERR_UNSUPPORTED
+    assert vrt.desc_check(vrt.lookahead_desc(16, 4, ring_slots=600)) == vrt.ERR_UNSUPPORTED   # not 64k
+    assert vrt.desc_check(vrt.lookahead_desc(16, 0)) == vrt.OK
+    assert [vrt.attn_out_frames(d, 0, n) for n in (1, 3, 4, 10)] == [0, 0, 1, 7]
+    assert [vrt.attn_out_frames(d, f, 4) for f in (1, 2, 3, 100)] == [2, 3, 4, 4]
+    assert vrt.attn_out_frames(vrt.lookahead_desc(16, 1), 0, 4) == 4
+    assert vrt.attn_out_frames(vrt.enc_desc(), 0, 4) == 4
+    assert all(vrt.attn_path(d, n) == 0 for n in (1, 4, 64, 512))
+    d3 = vrt.lookahead_desc(16, 4, n_layers=2)
+    ring = 2 * 8 * 576 * 64 * 2
+    assert vrt.state_device_bytes(d3) == 2 * (ring + 3 * 8 * 64 * 2)
+    base, nkv, nc = vrt.ring_advance(d3, 0, 0, 10)
+    assert (base, nkv, nc) == (0, 10, 0)
+    mixed = vrt.enc_desc()
+    mixed.lookahead = 4
+    assert vrt.desc_check(mixed) == vrt.ERR_INVALID        # lookahead belongs to ENC_LOOKAHEAD only
