@@ -392,6 +392,28 @@ __device__ __forceinline__ void dma16(const char* g, char* l) {
         : "v"((unsigned long long)(__UINTPTR_TYPE__)g), "s"(lds)
         : "memory");
 }
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (global_load_lds with saddr): no 64-bit address per lane.
+__device__ __forceinline__ void dma16s(const char* base, unsigned off, char* l) {
+    const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(__UINTPTR_TYPE__)l);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds)
+        : "memory");
+}
+// lane id read through volatile asm: recomputed where used instead of being
+// kept live (or spilled) across a loop
+__device__ __forceinline__ int lane_id_v() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 // wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -811,22 +833,23 @@ struct M4 {
     static constexpr int QW = 32;                 // queries per wave
     static constexpr int QT = 4 * QW;             // queries per workgroup
     static constexpr int TILE = kTile * RB;       // 8 KB
-    static constexpr int NST = 3;                 // LDS stages
+    static constexpr int NST = 2;                 // LDS stages (4 workgroups per CU fit)
     static constexpr int IPW = TILE / (4 * 1024); // DMA instructions per wave per K (or V) tile
     static constexpr int LPW = 2 * IPW;
     static constexpr int BYTES = NST * 2 * TILE;
 };
 static_assert(M4::QT == kQTileMfma, "query tile of the MFMA path");
+static_assert(M4::NST == 2, "the tile loop's DMA waits assume two stages");
 // A query's reference maximum moves only when a tile exceeds it by more than
 // this (log2 units), so unnormalised weights stay below 2^8.
 constexpr float kLazy = 8.0f;
 
-// max(a, b, c) in one instruction (operands are finite or the sentinel, so
-// no NaN handling is needed)
+// max(a, b, c); the compiler folds the pair into one v_max3_f32.  Written
+// with builtins, not inline asm, on purpose: the operands are often matrix-core
+// results, and only compiler-visible reads get the wait states the hardware
+// requires between an MFMA writing a register and a VALU reading it.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -835,7 +858,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
+// At most 128 VGPRs (four waves per SIMD), so four workgroups share a CU; the
+// tile loop works on one 32-key half-tile at a time to stay within them.
+__global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) {
     using L = M4;
     __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
     const int lane = threadIdx.x & 63;
@@ -886,12 +911,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
 #pragma unroll
         for (int i = 0; i < L::IPW; ++i) {
             const int ins = wave * L::IPW + i;
-            const int q = ins * 64 + lane;
+            const int q = ins * 64 + lane_id_v();
             const int r = q / L::CPR, pc = q % L::CPR;
             const int rr = min(max(r, rlo), rhi);
-            const long long off = (sb + rr) * L::RB;
-            dma16(Kg + off + 16 * (pc ^ ksw<L::CPR>(r)), ks + ins * 1024);
-            dma16(Vg + off + 16 * (pc ^ vsw<BF16T, L::CPR>(r)), vs + ins * 1024);
+            const unsigned off = (unsigned)rr * L::RB;
+            dma16s(Kg + sb * L::RB, off + 16 * (pc ^ ksw<L::CPR>(r)), ks + ins * 1024);
+            dma16s(Vg + sb * L::RB, off + 16 * (pc ^ vsw<BF16T, L::CPR>(r)), vs + ins * 1024);
         }
     };
 
@@ -933,7 +958,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
             cs[i] = r.c;
             sn[i] = r.s;
         }
-        if (ntt > 1) wait_vm<L::LPW * 2>(); else wait_vm<L::LPW>();
+        wait_vm<L::LPW>();   // the query loads (only tile 0 was issued after them)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const uint32_t* x0 = (const uint32_t*)&qraw[s];
@@ -960,7 +985,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
 
     // ---- bands relative to T0: the lane's query, and the wave's union /
     // intersection (for skipping and for mask-free half-tiles)
-    const int rlo_q = (int)(max(avail, pq - W + 1) - T0), rhi_q = (int)(pq - T0);
+    // the lane's own band [max(alo, h - W + 1), h] with h = hq0 + its query
+    // index is recomputed on the edge half-tiles that need it
+    const int hq0 = (int)(pq0 + qw0 - T0), alo = (int)(avail - T0);
     const long long wq_first = pq0 + qw0, wq_last = pq0 + qw0 + max(nqw, 1) - 1;
     const int blo = (int)(max(avail, wq_first - W + 1) - T0), bhi = (int)(wq_last - T0);
     const int flo = (int)(max(avail, wq_last - W + 1) - T0), fhi = (int)(wq_first - T0);
@@ -997,7 +1024,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
     constexpr uint32_t kOnes = 0x3f803f80u;   // (1, 1) in bf16
 
     for (int T = 0; T < ntt; ++T) {
-        if (T + 1 < ntt) wait_vm<L::LPW>(); else wait_vm<0>();
+        wait_vm<0>();   // two stages: only tile T is in flight here
         __syncthreads();
         if (T + L::NST - 1 < ntt) issue(T + L::NST - 1, (T + L::NST - 1) % L::NST);
         const char* Sb = lds + (T % L::NST) * 2 * L::TILE;   // K tile, then V tile
@@ -1010,107 +1037,73 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, StateTable t) {
             rel[k] = kb + 31 >= blo && kb <= bhi;
             full[k] = kb >= flo && kb + 31 <= fhi;
         }
-        // scores relative to the reference: S^T = [K | 1] [Q | -mref]^T
-        // both half-tiles' K operands first, then the two MFMA chains
-        // interleaved (each chain keeps its own k order)
-        f32x16_t s[2];
-        bf16x8_t kv[2][4];
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                kv[k][st] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(Sb + koff[st] + 32 * k * L::RB));
-        if (rel[0] && rel[1]) {
-#pragma unroll
-            for (int k = 0; k < 2; ++k)
-                s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, f32x16_t{}, 0, 0, 0);
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-#pragma unroll
-                for (int k = 0; k < 2; ++k)
-                    s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[k][st], qt[st], s[k], 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                if (!rel[k]) continue;
-                s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, f32x16_t{}, 0, 0, 0);
-#pragma unroll
-                for (int st = 0; st < 4; ++st)
-                    s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[k][st], qt[st], s[k], 0, 0, 0);
-            }
-        }
-        // mask (edge half-tiles only; masked scores become the sentinel, whose
-        // weight underflows to exactly 0) and the tile maximum
-        float mt = kSent;
+        // one 32-key half-tile at a time: scores, reference update, weights,
+        // then its share of the output
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             if (!rel[k]) continue;
+            // scores relative to the reference: S^T = [K | 1] [Q | -mref]^T
+            bf16x8_t kv[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                kv[st] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(Sb + koff[st] + 32 * k * L::RB));
+            f32x16_t s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, f32x16_t{}, 0, 0, 0);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[st], qt[st], s, 0, 0, 0);
+            // band mask on edge half-tiles (masked scores become the sentinel,
+            // whose weight underflows to exactly 0)
             if (!full[k]) {
+                const int bhi_v = hq0 + min(lane_id_v() & 31, nqw - 1);
+                const int blo_v = max(alo, bhi_v - W + 1);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = tb + 32 * k + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    s[k][r] = (key >= rlo_q && key <= rhi_q) ? s[k][r] : kSent;
+                    s[r] = (key >= blo_v && key <= bhi_v) ? s[r] : kSent;
                 }
             }
+            float mt = kSent;
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mt = max3f(mt, s[k][r], s[k][r + 1]);
-        }
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                             false, false);
-            mt = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), kSent);
-        }
-        const bool move = seen ? mt > kLazy : mt > kSent;
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {   // a query's first keys, or a jump of 2^kLazy
-            float delta = 0.f;
-            if (move) {
-                const float mnew = mref + mt;
-                const uint32_t hi = to_bf16(mnew);
-                const float mhi = __uint_as_float(hi << 16);
-                const uint32_t lo = to_bf16(mnew - mhi);
-                const float mt_ref = mhi + __uint_as_float(lo << 16);
-                const float alpha = seen ? fast_exp2(mref - mt_ref) : 0.f;
-                lpart *= alpha;
-#pragma unroll
-                for (int d = 0; d < 2; ++d)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-                delta = mt_ref - mref;
-                mref = mt_ref;
-                seen = true;
-                const uint32_t neg = (hi ^ 0x8000u) | ((lo ^ 0x8000u) << 16);
-                qext = __builtin_bit_cast(bf16x8_t, make_uint4(hf == 0 ? neg : 0u, 0u, 0u, 0u));
+            for (int r = 0; r < 16; r += 2) mt = max3f(mt, s[r], s[r + 1]);
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                                 false, false);
+                mt = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), kSent);
             }
+            const bool move = seen ? mt > kLazy : mt > kSent;
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {   // a query's first keys, or a jump of 2^kLazy
+                float delta = 0.f;
+                if (move) {
+                    const float mnew = mref + mt;
+                    const uint32_t hi = to_bf16(mnew);
+                    const float mhi = __uint_as_float(hi << 16);
+                    const uint32_t lo = to_bf16(mnew - mhi);
+                    const float mt_ref = mhi + __uint_as_float(lo << 16);
+                    const float alpha = seen ? fast_exp2(mref - mt_ref) : 0.f;
+                    lpart *= alpha;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                if (!rel[k]) continue;
+                    for (int d = 0; d < 2; ++d)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[k][r] -= delta;
+                        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+                    delta = mt_ref - mref;
+                    mref = mt_ref;
+                    seen = true;
+                    const uint32_t neg = (hi ^ 0x8000u) | ((lo ^ 0x8000u) << 16);
+                    qext = __builtin_bit_cast(bf16x8_t, make_uint4(hf == 0 ? neg : 0u, 0u, 0u, 0u));
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] -= delta;
             }
-        }
-        uint32_t pb[2][8];
+            uint32_t pb[8];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (!rel[k]) continue;
+            for (int w = 0; w < 8; ++w) pb[w] = pack_bf16x2(fast_exp2(s[2 * w]), fast_exp2(s[2 * w + 1]));
+            // the denominator sums the same bf16 weights the products use
 #pragma unroll
-            for (int w = 0; w < 8; ++w)
-                pb[k][w] = pack_bf16x2(fast_exp2(s[k][2 * w]), fast_exp2(s[k][2 * w + 1]));
-        }
-        // the denominator sums the same bf16 weights the products use
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (!rel[k]) continue;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) lpart = dot2bf(pb[k][w], kOnes, lpart);
-        }
-        // O^T += V^T P^T, key groups in ascending order
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (!rel[k]) continue;
+            for (int w = 0; w < 8; ++w) lpart = dot2bf(pb[w], kOnes, lpart);
+            // O^T += V^T P^T, key groups in ascending order
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const bf16x8_t pv = __builtin_bit_cast(
-                    bf16x8_t, make_uint4(pb[k][4 * c], pb[k][4 * c + 1], pb[k][4 * c + 2], pb[k][4 * c + 3]));
+                    bf16x8_t, make_uint4(pb[4 * c], pb[4 * c + 1], pb[4 * c + 2], pb[4 * c + 3]));
 #pragma unroll
                 for (int d = 0; d < 2; ++d) {
                     v4i16 part[2];
