@@ -900,6 +900,16 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
     const char* Kg = layer + (long long)g * a.g.slice_bytes;
     const char* Vg = Kg + a.g.v_off;
 
+    // the lane's 16-byte chunk of each DMA instruction: tile row r and its
+    // swizzled byte offset; kept for the tiles whose rows are all in range
+    unsigned dk[L::IPW], dv[L::IPW];
+#pragma unroll
+    for (int i = 0; i < L::IPW; ++i) {
+        const int q = (wave * L::IPW + i) * 64 + lane;
+        const int r = q / L::CPR, pc = q % L::CPR;
+        dk[i] = (unsigned)r * L::RB + 16 * (pc ^ ksw<L::CPR>(r));
+        dv[i] = (unsigned)r * L::RB + 16 * (pc ^ vsw<BF16T, L::CPR>(r));
+    }
     auto issue = [&](int T, int st) {
         const long long TB = T0 + (long long)T * kTile;
         // modulo ring: 0 <= TB < 2^31 and the slot count is a multiple of 64,
@@ -908,6 +918,16 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
         const int rlo = (int)max(0LL, wlo - TB), rhi = (int)min(63LL, whi - TB);
         char* ks = lds + st * 2 * L::TILE;
         char* vs = ks + L::TILE;
+        if (rlo == 0 && rhi == 63) {
+#pragma unroll
+            for (int i = 0; i < L::IPW; ++i) {
+                const int ins = wave * L::IPW + i;
+                dma16s(Kg + sb * L::RB, dk[i], ks + ins * 1024);
+                dma16s(Vg + sb * L::RB, dv[i], vs + ins * 1024);
+            }
+            return;
+        }
+        // an edge tile: rows outside [rlo, rhi] repeat the nearest row in range
 #pragma unroll
         for (int i = 0; i < L::IPW; ++i) {
             const int ins = wave * L::IPW + i;
