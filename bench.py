@@ -641,6 +641,7 @@ def cpu_baseline_conv(steps: int):
 
 KERNEL_SRC = os.path.join(ROOT, "sliding_window_cached_amd", "csrc", "vrt_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+MFMA_BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy.txt")
 
 
 def kernels_sha256() -> str:
@@ -675,6 +676,21 @@ def measured_traffic(kernel: str, workload: str):
         if len(f) == 5 and f[0] == kernel and f[1] == workload and f[4] == f"kernels_sha256={sha}":
             return {"fetch_bytes": float(f[2]), "write_bytes": float(f[3]),
                     "bytes": float(f[2]) + float(f[3])}
+    return None
+
+
+def measured_mfma_busy(kernel: str, workload: str):
+    """Fraction of the launch the matrix cores were busy, from the rocprofv3
+    SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE run recorded in
+    profiles/mfma_busy.txt, or None when no record exists or the kernel
+    source changed since it was taken."""
+    if not os.path.exists(MFMA_BUSY_FILE):
+        return None
+    sha = kernels_sha256()
+    for line in open(MFMA_BUSY_FILE):
+        f = line.split()
+        if len(f) == 4 and f[0] == kernel and f[1] == workload and f[3] == f"kernels_sha256={sha}":
+            return float(f[2])
     return None
 
 
@@ -928,8 +944,11 @@ def bench_c3(args):
             "launches_timed": len(attn_ms),
             "hbm_achieved_gbs": gbs,
             "hbm_frac": gbs / HBM_PEAK_GBS,
+            "mfma_busy_counter": measured_mfma_busy("k_attn_mfma", workload_key(args, "c3")),
             "note": "algorithmic flops = 4*d*H per (query, visible key); the kernel is "
-                    "HBM-bound at the roofline (about 216 flop/B < the 312 flop/B ridge)",
+                    "HBM-bound at the roofline (about 216 flop/B < the 312 flop/B ridge); "
+                    "mfma_busy_counter = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 "
+                    "SIMDs) from the rocprofv3 counter run of the same workload",
         },
     }
 
