@@ -257,19 +257,28 @@ using G64x128 = GT<64, 128, 3>;
 using G64 = GT<64, 64, 4>;
 
 // ------------------------------------------------------- conv stem rows ----
-// One workgroup per (stem, row): 16-byte chunks between a stem's cache rows
-// and its staging rows; a fresh stem's cache reads as zeros (the causal
-// left padding).
+// One workgroup per (segment, stem, row): 16-byte chunks between a stem's
+// cache rows (or the new input rows) and its staging rows; a fresh stem's
+// cache reads as zeros (the causal left padding).  Segments are laid out one
+// after the other over the grid.
 __global__ __launch_bounds__(64) void k_row_copy(RowCopyArgs a, RowCopyTable t) {
-    const int g = blockIdx.x / a.rows, r = blockIdx.x - g * a.rows;
-    char* st = a.stage + ((long long)g * a.gstride + a.off + r) * a.row_bytes;
-    char* ca = (char*)t.cache[g] + (long long)r * a.row_bytes;
-    for (int c = threadIdx.x; c < a.row_bytes / 16; c += blockDim.x) {
-        if (a.to_cache) {
-            *(uint4*)(ca + 16 * c) = *(const uint4*)(st + 16 * c);
+    int b = blockIdx.x, si = 0;
+    while (si + 1 < a.n_seg && b >= a.n_groups * a.seg[si].rows) {
+        b -= a.n_groups * a.seg[si].rows;
+        ++si;
+    }
+    const RowCopySeg& sg = a.seg[si];
+    const int g = b / sg.rows, r = b - g * sg.rows;
+    char* st = sg.stage + ((long long)g * sg.gstride + sg.off + r) * sg.row_bytes;
+    const char* src = sg.src ? sg.src + ((long long)g * sg.src_gstride + r) * sg.row_bytes
+                             : (const char*)t.cache[g] + sg.cache_off + (long long)r * sg.row_bytes;
+    for (int c = threadIdx.x; c < sg.row_bytes / 16; c += blockDim.x) {
+        if (sg.to_cache) {
+            *(uint4*)((char*)t.cache[g] + sg.cache_off + (long long)r * sg.row_bytes + 16 * c) =
+                *(const uint4*)(st + 16 * c);
         } else {
-            const uint4 v = (a.zero_from_cache && t.fresh[g]) ? make_uint4(0, 0, 0, 0)
-                                                             : *(const uint4*)(ca + 16 * c);
+            const uint4 v = (!sg.src && sg.zero_fresh && t.fresh[g]) ? make_uint4(0, 0, 0, 0)
+                                                                    : *(const uint4*)(src + 16 * c);
             *(uint4*)(st + 16 * c) = v;
         }
     }
@@ -313,10 +322,18 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, hipS
 }
 
 hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s) {
-    if (a.n_groups < 1 || a.n_groups > kMaxStems || a.rows < 0 || a.row_bytes < 16 || a.row_bytes % 16)
+    if (a.n_groups < 1 || a.n_groups > kMaxStems || a.n_seg < 1 || a.n_seg > kMaxCopySeg)
         return hipErrorInvalidValue;
-    if (a.rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_row_copy, dim3((unsigned)(a.n_groups * a.rows)), dim3(64), 0, s, a, t);
+    long long blocks = 0;
+    for (int i = 0; i < a.n_seg; ++i) {
+        const RowCopySeg& g = a.seg[i];
+        if (g.rows < 0 || g.row_bytes < 16 || g.row_bytes % 16 || !g.stage || (g.to_cache && g.src))
+            return hipErrorInvalidValue;
+        blocks += (long long)a.n_groups * g.rows;
+    }
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_row_copy, dim3((unsigned)blocks), dim3(64), 0, s, a, t);
     return hipGetLastError();
 }
 

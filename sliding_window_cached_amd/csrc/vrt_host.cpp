@@ -939,7 +939,9 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
     std::vector<const vrt_conv_stem*> seen;
     for (int i = 0; i < n_stems; ++i) {
         const vrt_conv_stem* c = stems[i];
-        if (!c || c->n_mel != n_mel || c->d_model != d || c->pending != p) return VRT_ERR_INVALID;
+        if (!c || c->n_mel != n_mel || c->d_model != d || c->pending != p ||
+            c->pend_off != stems[0]->pend_off)
+            return VRT_ERR_INVALID;
         seen.push_back(c);
     }
     std::sort(seen.begin(), seen.end());
@@ -953,27 +955,24 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
     const int L = p + n_frames, o = conv1_outputs(L), keep = L - 2 * o;   // keep: 1 or 2
     char* st0 = (char*)workspace;                       // [stem][n_frames + 2][n_mel]
     char* st1 = st0 + pad256((size_t)n_stems * (n_frames + kConvPad0) * n_mel * 2);  // [stem][n_frames + 2][d]
-    RowCopyTable t0, t1;
+    RowCopyTable t;
     for (int i = 0; i < n_stems; ++i) {
-        t0.cache[i] = (unsigned long long)(uintptr_t)stems[i]->dev;
-        t1.cache[i] = (unsigned long long)(uintptr_t)(stems[i]->dev + stems[i]->pend_off);
-        t0.fresh[i] = t1.fresh[i] = stems[i]->fresh ? 1 : 0;
+        t.cache[i] = (unsigned long long)(uintptr_t)stems[i]->dev;
+        t.fresh[i] = stems[i]->fresh ? 1 : 0;
     }
+    const long long pend_off = (long long)stems[0]->pend_off;
     clear_sticky_error();
-    auto copy = [&](const RowCopyTable& t, char* stage, long long gstride, long long off, int rows,
-                    int row_bytes, int to_cache) {
-        RowCopyArgs a{n_stems, rows, row_bytes, to_cache, stage, gstride, off, 1};
-        return note(launch_row_copy(a, t, stream));
-    };
-    // staging: [mel cache | new mel] and [pending conv0 rows | conv0 output]
-    if (copy(t0, st0, n_frames + kConvPad0, 0, kConvPad0, n_mel * 2, 0) != hipSuccess ||
-        copy(t1, st1, L, 0, p, d * 2, 0) != hipSuccess)
-        return VRT_ERR_DEVICE;
-    // the new mel rows go behind each stem's cache rows (one strided copy)
-    if (note(hipMemcpy2DAsync(st0 + (size_t)kConvPad0 * n_mel * 2, (size_t)(n_frames + kConvPad0) * n_mel * 2,
-                              mel, (size_t)n_frames * n_mel * 2, (size_t)n_frames * n_mel * 2, n_stems,
-                              hipMemcpyDeviceToDevice, stream)) != hipSuccess)
-        return VRT_ERR_DEVICE;
+    // staging, in one launch: [mel cache | new mel] and [pending conv0 rows | conv0 output]
+    {
+        RowCopyArgs a{};
+        a.n_groups = n_stems;
+        a.n_seg = 3;
+        a.seg[0] = RowCopySeg{kConvPad0, n_mel * 2, 0, st0, n_frames + kConvPad0, 0, 0, nullptr, 0, 1};
+        a.seg[1] = RowCopySeg{p, d * 2, 0, st1, L, 0, pend_off, nullptr, 0, 1};
+        a.seg[2] = RowCopySeg{n_frames, n_mel * 2, 0, st0, n_frames + kConvPad0, kConvPad0, 0,
+                              (const char*)mel, n_frames, 0};
+        if (note(launch_row_copy(a, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    }
     GemmArgs g0{};
     g0.A = st0;
     g0.lda = n_mel;
@@ -1015,11 +1014,15 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
         g1.seg[0] = GemmSeg{out, w->b1, d};
         if (note(launch_gemm(g1, stream)) != hipSuccess) return VRT_ERR_DEVICE;
     }
-    // new caches: the last two staged mel rows; the conv0 rows from 2 o on
-    for (int i = 0; i < n_stems; ++i) t0.fresh[i] = t1.fresh[i] = 0;
-    if (copy(t0, st0, n_frames + kConvPad0, n_frames, kConvPad0, n_mel * 2, 1) != hipSuccess ||
-        copy(t1, st1, L, 2 * o, keep, d * 2, 1) != hipSuccess)
-        return VRT_ERR_DEVICE;
+    // new caches, in one launch: the last two staged mel rows; the conv0 rows from 2 o on
+    {
+        RowCopyArgs a{};
+        a.n_groups = n_stems;
+        a.n_seg = 2;
+        a.seg[0] = RowCopySeg{kConvPad0, n_mel * 2, 1, st0, n_frames + kConvPad0, n_frames, 0, nullptr, 0, 0};
+        a.seg[1] = RowCopySeg{keep, d * 2, 1, st1, L, 2LL * o, pend_off, nullptr, 0, 0};
+        if (note(launch_row_copy(a, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    }
     for (int i = 0; i < n_stems; ++i) {
         stems[i]->pending = keep;
         stems[i]->fresh = false;

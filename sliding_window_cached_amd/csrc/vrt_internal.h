@@ -180,18 +180,27 @@ inline void gemm_plain(GemmArgs* g) {
 }
 
 // ---- causal conv stem (vrt_block.hip): row copies between each stem's
-// caches (device memory of its own, given by a table) and the staging rows
+// caches (device memory of its own, given by a table), the new input rows and
+// the staging rows; up to kMaxCopySeg segments in one launch
 constexpr int kMaxStems = 256;
-struct RowCopyArgs {
-    int n_groups, rows;         // copy `rows` rows for each of n_groups stems
+constexpr int kMaxCopySeg = 3;
+struct RowCopySeg {
+    int rows;                   // rows per group (0: the segment is empty)
     int row_bytes;              // multiple of 16
-    int to_cache;               // 0: cache -> staging; 1: staging -> cache
-    char* stage;                // staging rows: group g row r at stage + (g gstride + off + r) row_bytes
+    int to_cache;               // 0: cache (or src) -> staging; 1: staging -> cache
+    char* stage;                // group g row r at stage + (g gstride + off + r) row_bytes
     long long gstride, off;
-    int zero_from_cache;        // cache -> staging: write zeros for groups marked fresh
+    long long cache_off;        // byte offset of the segment's rows in each stem's memory
+    const char* src;            // to_cache = 0 and non-null: group g row r read from
+    long long src_gstride;      //   src + (g src_gstride + r) row_bytes instead of a cache
+    int zero_fresh;             // cache -> staging: zeros for the stems marked fresh
+};
+struct RowCopyArgs {
+    int n_groups, n_seg;
+    RowCopySeg seg[kMaxCopySeg];
 };
 struct RowCopyTable {
-    unsigned long long cache[kMaxStems];   // row 0 of each stem's cache rows
+    unsigned long long cache[kMaxStems];   // base of each stem's memory
     int fresh[kMaxStems];
 };
 hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s);
