@@ -837,6 +837,29 @@ def bench_c1(args):
     }
 
 
+def mfma_band(avail: int, p0: int, n: int, qtile: int = 128, qw: int = 32):
+    """(visible, computed) (query, key) pairs of one unit's matrix-core
+    attention: visible = the keys in each query's window; computed = the
+    32-key x 32-query blocks the kernel runs, a wave skipping the half-tiles
+    of the absolute 64-key grid that hold no key of any of its queries."""
+    visible = sum(q - max(avail, q - W + 1) + 1 for q in range(p0, p0 + n))
+    computed = 0
+    for qc in range((n + qtile - 1) // qtile):
+        pq0 = p0 + qc * qtile
+        nq = min(qtile, n - qc * qtile)
+        wlo, whi = max(avail, pq0 - W + 1), pq0 + nq - 1
+        t0 = (wlo // 64) * 64
+        for w0 in range(0, nq, qw):
+            first, last = pq0 + w0, pq0 + min(nq, w0 + qw) - 1
+            blo, bhi = max(avail, first - W + 1) - t0, last - t0
+            kb = 0
+            while kb <= whi - t0:
+                if kb + 31 >= blo and kb <= bhi:
+                    computed += 32 * qw
+                kb += 32
+    return visible, computed
+
+
 def c3_schedule(T=15300, B=512):
     return [min(B, T - t) for t in range(0, T, B)]
 
@@ -879,7 +902,7 @@ def bench_c3(args):
     for j in range(args.steps):
         m = sched[bb]
         base, nkv_after, _ = vrt.ring_advance(desc, base, nkv, m)
-        plan.append((bb, m, nkv_after - m))
+        plan.append((bb, m, nkv_after - m, base))
         nkv = nkv_after
         bb += 1
         if bb == len(sched):
@@ -889,7 +912,7 @@ def bench_c3(args):
     log(f"c3: timing {args.steps} batches")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for j, (bj, m, _) in enumerate(plan):
+    for j, (bj, m, _, _) in enumerate(plan):
         vrt.set_attn_events(ev[j][0], ev[j][1])
         feed(bj)
         if bj == len(sched) - 1:
@@ -900,14 +923,15 @@ def bench_c3(args):
     attn_ms = [a.elapsed_time(b) for a, b in ev]
     st.close()
 
-    frames = sum(m for _, m, _ in plan)
-    work = [attn_work(k, m) for _, m, k in plan]
+    frames = sum(m for _, m, _, _ in plan)
+    work = [attn_work(k, m) for _, m, k, _ in plan]
+    band = [mfma_band(base, base + k, m) for _, m, k, base in plan]
     nbytes = sum(L * w[0] for w in work)
     flops = sum(L * w[1] for w in work)
     t_attn = sum(attn_ms) * 1e-3
     tflops = flops / t_attn / 1e12
     gbs = nbytes / t_attn / 1e9
-    full = [(a, L * attn_work(k, m)[1]) for a, (_, m, k) in zip(attn_ms, plan) if m == 512 and k >= W]
+    full = [(a, L * attn_work(k, m)[1]) for a, (_, m, k, _) in zip(attn_ms, plan) if m == 512 and k >= W]
     return {
         "metric": METRIC,
         "value": frames / wall,
@@ -945,10 +969,12 @@ def bench_c3(args):
             "hbm_achieved_gbs": gbs,
             "hbm_frac": gbs / HBM_PEAK_GBS,
             "mfma_busy_counter": measured_mfma_busy("k_attn_mfma", workload_key(args, "c3")),
+            "band_efficiency": sum(v for v, _ in band) / sum(c for _, c in band),
             "note": "algorithmic flops = 4*d*H per (query, visible key); the kernel is "
                     "HBM-bound at the roofline (about 216 flop/B < the 312 flop/B ridge); "
                     "mfma_busy_counter = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 "
-                    "SIMDs) from the rocprofv3 counter run of the same workload",
+                    "SIMDs) from the rocprofv3 counter run of the same workload; band_efficiency = "
+                    "visible (query, key) pairs / pairs in the 32 x 32 score blocks the kernel computes",
         },
     }
 
