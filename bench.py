@@ -138,7 +138,7 @@ def cpu_baseline_block(steps: int):
                       f"oracle.stream.EncStream in fp64 numpy, {el:.1f} s"}
 
 
-def cpu_baseline_dec(contexts, steps: int = 20):
+def cpu_baseline_dec(contexts, steps: int = 80):
     """The fp64 oracle's decoder stream (oracle.stream.DecStream) on a bounded
     sample: one layer of one stream at the median context, `steps` timed
     single-token steps after an untimed fill; scaled to tokens/s through 26
@@ -595,10 +595,11 @@ def bench_cm(args):
     }
 
 
-def cpu_baseline_cm(steps: int):
+def cpu_baseline_cm(steps: int, passes: int = 1):
     """The fp64 oracle (oracle.attention.lookahead over the frames seen so
     far, the answered rows only) for one stream through one (16,4) layer, 4
-    frames per feed; scaled to the six layers of the workload."""
+    frames per feed, the same `steps` feeds timed `passes` times (the inputs
+    stay small); scaled to the six layers of the workload."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import attention
@@ -609,12 +610,13 @@ def cpu_baseline_cm(steps: int):
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        for i in range(steps):          # a feed of 4 frames answers 4 queries, 3 frames back
-            for t in range(16 + 4 * i, 16 + 4 * i + 4):
-                attention.window_rows(q[t], k[t - 15:t + 4], v[t - 15:t + 4], 1)
+        for _ in range(passes):
+            for i in range(steps):          # a feed of 4 frames answers 4 queries, 3 frames back
+                for t in range(16 + 4 * i, 16 + 4 * i + 4):
+                    attention.window_rows(q[t], k[t - 15:t + 4], v[t - 15:t + 4], 1)
         el = time.perf_counter() - t0
-    return {"value": 4 * steps / el / 6, "unit": "frames/s", "cores": 1, "kind": "oracle",
-            "sample": f"one stream, one (16,4) layer, {steps} feeds of 4 frames; each answered query "
+    return {"value": 4 * steps * passes / el / 6, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"one stream, one (16,4) layer, {steps} feeds of 4 frames timed {passes} times; each answered query "
                       f"over its window (oracle.attention.window_rows, fp64 numpy, one thread), "
                       f"{el:.1f} s; divided by 6 layers"}
 
@@ -1162,18 +1164,18 @@ def main():
         log("cpu baseline: timing the fp64 oracle on a bounded sample")
         from synth import offsets
         if args.config == "c2":
-            res["cpu_baseline"] = cpu_baseline(1, 1, W, 400, 4, 0.5, offsets(2, 1, 10 ** 4, 10 ** 6),
+            res["cpu_baseline"] = cpu_baseline(1, 1, W, 1000, 4, 0.5, offsets(2, 1, 10 ** 4, 10 ** 6),
                                                "steady-state sample")
         elif args.config == "c2b":
-            res["cpu_baseline"] = cpu_baseline_block(60)
+            res["cpu_baseline"] = cpu_baseline_block(750)
         elif args.config == "cs":
-            res["cpu_baseline"] = cpu_baseline_conv(40)
+            res["cpu_baseline"] = cpu_baseline_conv(450)
         elif args.config == "cm":
-            res["cpu_baseline"] = cpu_baseline_cm(10000)
+            res["cpu_baseline"] = cpu_baseline_cm(10000, passes=8)
         elif args.config == "c1":
-            res["cpu_baseline"] = cpu_baseline(1, 32, W, 400, 4, 0.5, [0], "staggered-streams sample")
+            res["cpu_baseline"] = cpu_baseline(1, 32, W, 1000, 4, 0.5, [0], "staggered-streams sample")
         elif args.config == "c3":
-            res["cpu_baseline"] = cpu_baseline(1, 32, 0, 4, 512, 1.0, [0], "catch-up sample")
+            res["cpu_baseline"] = cpu_baseline(1, 32, 0, 10, 512, 1.0, [0], "catch-up sample")
         else:
             res["cpu_baseline"] = cpu_baseline_dec(res["config"]["contexts"])
     print(json.dumps(res), flush=True)
