@@ -573,15 +573,19 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
                 at.n_splits = 1;
                 at.split_len = kSplitLen;
                 at.scale_log2 = scale_log2(g.D);
-                at.append = 0;
                 at.qchunk = kRows / g.group;
                 at.n_qchunks = (n_out_sb + at.qchunk - 1) / at.qchunk;
+                // with one query chunk the attention launch appends the new
+                // rows itself; otherwise (or with no query to answer) a
+                // separate append runs first
+                at.append = at.n_qchunks == 1 ? 1 : 0;
+                at.look_keep = at.append ? keep : 0;   // and saves the waiting rows
                 at.hg = n_out_sb > 0 ? pick_hg(g, (long long)um.n_states * um.nl,
                                                std::min(at.qchunk, n_out_sb) * g.group, at.n_qchunks, 1)
                                      : 1;
-                if (note(launch_rope_append(aa, t, stream)) != hipSuccess ||
+                if ((!at.append && note(launch_rope_append(aa, t, stream)) != hipSuccess) ||
                     (n_out_sb > 0 && note(launch_attn(at, false, t, stream)) != hipSuccess) ||
-                    note(launch_pend_save(at, t, keep, stream)) != hipSuccess) {
+                    (!at.append && note(launch_pend_save(at, t, keep, stream)) != hipSuccess)) {
                     poison(st, n_states);
                     return VRT_ERR_DEVICE;
                 }

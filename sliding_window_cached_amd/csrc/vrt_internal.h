@@ -109,6 +109,9 @@ struct AttnArgs {
     // rows when i < look_pend, else from new frame i - look_pend; its output
     // goes to row look_o0 + i of the call's output
     int look_f, look_pend, look_nout, look_o0;
+    // > 0: the launch (one query chunk) also leaves the last look_keep rows of
+    // [waiting rows | new q rows] as the next call's waiting rows
+    int look_keep;
     long long pend_off;       // byte offset, in a state, of layer 0's waiting q rows
     long long pend_layer;     // bytes of one layer's waiting rows (look_f rows)
 };

@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
             src = (const char*)a.q + ((cu * m.n_total + frame) * qrow + (long long)(g * group + gh) * D) * E::E;
         ld4<E>(src + 4 * c * E::E, it.x0);
         ld4<E>(src + (H2 + 4 * c) * E::E, it.x1);
-        if (APPEND && appender && gh == 0) {
+        if (APPEND && !LOOK && appender && gh == 0) {
             const long long kv0 = ((cu * m.n_total + frame) * krow + (long long)g * D) * E::E;
             ld4<E>((const char*)a.k + kv0 + 4 * c * E::E, it.k0);
             ld4<E>((const char*)a.k + kv0 + (H2 + 4 * c) * E::E, it.k1);
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         char* dst = Qs + (hh * R + r) * L::RB;
         st4<E, false>(dst + 4 * c * E::E, y0);
         st4<E, false>(dst + (H2 + 4 * c) * E::E, y1);
-        if (APPEND && appender && gh == 0) {
+        if (APPEND && !LOOK && appender && gh == 0) {
             char* Kg = layer + (long long)g * a.g.slice_bytes;
             char* Vg = Kg + a.g.v_off;
             const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + j);
@@ -615,8 +615,48 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         load_item(x, more);
         finish_item(x, more);
     }
+    // (left, right) windows: the answered queries lag the new frames, so the
+    // new K/V rows (copied unrotated, as the separate append writes them) are
+    // their own items
+    if constexpr (LOOK && APPEND) {
+        if (appender) {
+            const int nrow = hg * m.n * L::CPR;
+            for (int x = threadIdx.x; x < nrow; x += blockDim.x) {
+                const int c = x % L::CPR, f = (x / L::CPR) % m.n, hh = x / (L::CPR * m.n);
+                const int g = g0 + hh;
+                const long long slot = MOD ? ((t.p0[si] + f) % a.g.slots) : (long long)(nkv + f);
+                const long long src = ((cu * m.n_total + m.t0 + f) * krow + (long long)g * D) * E::E + 16 * c;
+                char* kd = layer + (long long)g * a.g.slice_bytes + slot * L::RB + 16 * c;
+                const uint4 kk = gld<uint4>((const char*)a.k + src);
+                const uint4 vv = gld<uint4>((const char*)a.v + src);
+                gst<uint4>(kd, kk);
+                gst<uint4>(kd + a.g.v_off, vv);
+            }
+        }
+    }
     // appended rows visible to every thread's later loads; Qs written
     __syncthreads();
+    // the next call's waiting q rows, for this group's heads: one 16-byte
+    // column per thread, rows in ascending order (a row is written only after
+    // every row it is read from, so the copy is safe in place); the prologue
+    // has read the old waiting rows before the barrier
+    if constexpr (LOOK) {
+        if (a.look_keep > 0 && qc == 0) {
+            const long long rowb = (long long)a.g.hq * D * E::E;
+            const int c0 = g0 * group * D * E::E / 16, nc = hg * group * D * E::E / 16;
+            char* pend = (char*)t.ring[si] + a.pend_off + (long long)(m.layer0 + m.l_off + li) * a.pend_layer;
+            const int p = a.look_pend, keep = a.look_keep, shift = p + m.n - keep;
+            for (int c = threadIdx.x; c < nc; c += blockDim.x)
+                for (int r = 0; r < keep; ++r) {
+                    const int src = shift + r;
+                    const uint4 v =
+                        src < p ? gld<uint4>(pend + src * rowb + 16 * (c0 + c))
+                                : gld<uint4>((const char*)a.q + (cu * m.n_total + m.t0 + (src - p)) * rowb +
+                                             16 * (c0 + c));
+                    gst<uint4>(pend + r * rowb + 16 * (c0 + c), v);
+                }
+        }
+    }
 #pragma unroll
     for (int st = 0; st < PRE; ++st)
         if (st < ntt && !pre_done[st]) issue(st, st);
@@ -1273,17 +1313,20 @@ hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t 
         else                                                                                        \
             hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, kRows / 4, false>), grid, block, 0, s, a, t); \
     } while (0)
-#define VRT_LOOK(MOD)                                                                               \
+#define VRT_LOOK(MOD, APP)                                                                          \
     do {                                                                                            \
         if (one)                                                                                    \
-            hipLaunchKernelGGL((k_attn<E_, D_, MOD, false, false, 1, true>), grid, block, 0, s, a, t); \
+            hipLaunchKernelGGL((k_attn<E_, D_, MOD, false, APP, 1, true>), grid, block, 0, s, a, t); \
         else                                                                                        \
-            hipLaunchKernelGGL((k_attn<E_, D_, MOD, false, false, kRows / 4, true>), grid, block, 0, s, a, t); \
+            hipLaunchKernelGGL((k_attn<E_, D_, MOD, false, APP, kRows / 4, true>), grid, block, 0, s, a, t); \
     } while (0)
-    if (!a.g.rope && (split || app)) return hipErrorInvalidValue;
+    // windows without rotation: no splits; the fused append needs one query chunk
+    if (!a.g.rope && (split || (app && a.n_qchunks != 1))) return hipErrorInvalidValue;
     VRT_DISPATCH_ED(a.g.dtype, a.g.D, {
-        if (!a.g.rope && a.g.mod) VRT_LOOK(true);
-        else if (!a.g.rope) VRT_LOOK(false);
+        if (!a.g.rope && a.g.mod && app) VRT_LOOK(true, true);
+        else if (!a.g.rope && a.g.mod) VRT_LOOK(true, false);
+        else if (!a.g.rope && app) VRT_LOOK(false, true);
+        else if (!a.g.rope) VRT_LOOK(false, false);
         else if (a.g.mod && split && app) VRT_ATTN(true, true, true);
         else if (a.g.mod && split) VRT_ATTN(true, true, false);
         else if (a.g.mod && app) VRT_ATTN(true, false, true);
