@@ -1116,8 +1116,8 @@ def main():
                     help="c2: record the attention-kernel events on every N-th timed step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: streams are independent and would shard across "
-              "GPUs with no exchange, but this build runs and reports a single GPU.",
+        print("bench.py measures one GPU only (--gpus 1): streams are independent and would "
+              "shard across GPUs with no exchange; a single GPU is run and reported.",
               file=sys.stderr)
         sys.exit(2)
     if args.config == "copy":

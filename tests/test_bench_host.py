@@ -44,3 +44,14 @@ def test_band_full_window_value():
     # 512 queries with 749 old keys: 0.9375 of the computed pairs are visible
     v, c = bench.mfma_band(1000, 1750, 512)
     assert (v, c) == (384000, 409600)
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
