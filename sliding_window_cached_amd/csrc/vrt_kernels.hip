@@ -382,7 +382,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // The loads carry the non-temporal hint: the vector kernel reads each window
 // row once per launch, and streaming them past the caches' retention raised
 // the serving step from 66.8 % to 69.9 % and the decode step from 68.3 % to
-// 76.1 % of peak HBM bandwidth (same part, same session).
+// 76.1 % of peak HBM bandwidth (measured back to back on one MI355X).
 __device__ __forceinline__ void dma16(const char* g, char* l) {
     const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(__UINTPTR_TYPE__)l);
     unsigned saved;
@@ -855,9 +855,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
 // such a half-tile would only add zero weights.  The softmax scale is folded
 // into the rotated query, so scores come out in log2 units, and the matrix
 // cores also subtract a per-query reference maximum (an extra k-step), which
-// moves only when a tile exceeds it by more than 2^8 (then the accumulators
-// are rescaled), so most tiles need neither a subtraction nor a rescale on
-// the vector ALU.  The denominator sums the bf16 weights the products use.
+// moves only when a half-tile's scores exceed it by more than 2^8 (then the
+// accumulators are rescaled), so most half-tiles need neither a subtraction
+// nor a rescale on the vector ALU.  The denominator sums the bf16 weights the products use.
 // Every per-query step (the MFMA chains, the reference, the partial sums,
 // the rescale) depends only on that query's own window and the absolute tile
 // grid, so the result does not depend on how frames were batched.
@@ -884,8 +884,8 @@ struct M4 {
 };
 static_assert(M4::QT == kQTileMfma, "query tile of the MFMA path");
 static_assert(M4::NST == 2, "the tile loop's DMA waits assume two stages");
-// A query's reference maximum moves only when a tile exceeds it by more than
-// this (log2 units), so unnormalised weights stay below 2^8.
+// A query's reference maximum moves only when a half-tile's scores exceed it
+// by more than this (log2 units), so unnormalised weights stay below 2^8.
 constexpr float kLazy = 8.0f;
 
 // max(a, b, c); the compiler folds the pair into one v_max3_f32.  Written
@@ -1066,7 +1066,7 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
     // multiplies the constant operand kext (ones at k = 0, 1) with qext =
     // (-m_hi, -m_lo), the reference split into two bf16 values, so the block
     // comes out as s - mref with mref = m_hi + m_lo exactly.  mref is 0 until
-    // the query's first visible key, then moves only when a tile's maximum
+    // the query's first visible key, then moves only when a half-tile's maximum
     // exceeds it by more than kLazy (weights stay below 2^kLazy); a lane whose
     // reference does not move is rescaled by exactly 1, if at all.
     // lane parts of the LDS addresses (the swizzles depend only on lane
