@@ -124,8 +124,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int ntn = a.N / L::BN;
-    const int m0 = (blockIdx.x / ntn) * L::BM, n0 = (blockIdx.x % ntn) * L::BN;
-    const int nk = a.K / L::BK;
+    const int ntiles = (int)(gridDim.x / a.ksplit);
+    const int ks = blockIdx.x / ntiles, tile = blockIdx.x - ks * ntiles;   // k part, output tile
+    const int m0 = (tile / ntn) * L::BM, n0 = (tile % ntn) * L::BN;
+    const int nk = a.K / L::BK / a.ksplit;                                 // k steps of this part
+    const int kt0 = ks * nk;
     const char* A = (const char*)a.A;
     const char* W = (const char*)a.W;
 
@@ -138,7 +141,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         const int g = m / a.a_grp, li = m - g * a.a_grp;
         arow[i] = (long long)g * a.a_gstride + (long long)li * a.a_stride;
     }
-    auto issue = [&](int kt, int st) {
+    auto issue = [&](int kl, int st) {
+        const int kt = kt0 + kl;
         char* as = lds + st * L::STAGE;
         char* ws = as + L::ATILE;
         const long long kb = (long long)kt * L::BK * 2;
@@ -220,6 +224,21 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 
     // epilogue: lane l, register r of block (i, j) holds row
     // 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32 of the block
+    if (a.ksplit > 1) {   // fp32 sums of this k part; the reduce finishes them
+        float* pp = a.part + (long long)ks * a.M * a.N;
+#pragma unroll
+        for (int j = 0; j < L::JB; ++j) {
+            const int col = n0 + (L::BN / 2) * wn + 32 * j + lr;
+#pragma unroll
+            for (int i = 0; i < L::IB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + (L::BM / 2) * wm + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (row < a.M) pp[(long long)row * a.N + col] = acc[i][j][r];
+                }
+        }
+        return;
+    }
     const int seg = n0 / a.seg_w;
     char* out = (char*)a.seg[seg].out;
     const char* bias = (const char*)a.seg[seg].bias;
@@ -245,6 +264,42 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
                 *(uint16_t*)(out + (orow * ldo + lc) * 2) = to_bf16(v);
             }
     }
+}
+
+// Ordered reduce of a split product: one thread per (row, 4 columns); the
+// parts are added in ascending order, then bias, residual and activation as
+// in the one-pass epilogue, rounded once to bf16.
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a) {
+    const long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int nq = a.N / 4;
+    if (x >= (long long)a.M * nq) return;
+    const int row = (int)(x / nq), col = (int)(x - (long long)row * nq) * 4;
+    const long long mn = (long long)a.M * a.N, o = (long long)row * a.N + col;
+    float4 v = *(const float4*)(a.part + o);
+    for (int s = 1; s < a.ksplit; ++s) {
+        const float4 w = *(const float4*)(a.part + s * mn + o);
+        v.x = v.x + w.x; v.y = v.y + w.y; v.z = v.z + w.z; v.w = v.w + w.w;
+    }
+    const int seg = col / a.seg_w, lc = col - seg * a.seg_w;
+    char* out = (char*)a.seg[seg].out;
+    const char* bias = (const char*)a.seg[seg].bias;
+    float t[4] = {v.x, v.y, v.z, v.w};
+    uint16_t y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        float w = t[u] + (bias ? __uint_as_float((uint32_t)*(const uint16_t*)(bias + 2 * (lc + u)) << 16) : 0.f);
+        if (a.R)
+            w += __uint_as_float(
+                (uint32_t)*(const uint16_t*)((const char*)a.R + ((long long)row * a.ldr + col + u) * 2) << 16);
+        if (a.act == 1) w = 0.5f * w * (1.0f + erff(w * 0.70710678118654752f));
+        y[u] = to_bf16(w);
+    }
+    const int og = row / a.o_grp;
+    const long long orow = (long long)og * a.o_gstride + (row - og * a.o_grp) + a.o_off;
+    uint2 pk;
+    pk.x = (uint32_t)y[0] | ((uint32_t)y[1] << 16);
+    pk.y = (uint32_t)y[2] | ((uint32_t)y[3] << 16);
+    *(uint2*)(out + (orow * a.seg[seg].ld + lc) * 2) = pk;
 }
 
 // Tile shapes, largest first: 128 x 128 with 3 tiles in flight (one
@@ -354,23 +409,31 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.M < 1 || a.N < 128 || a.N % 128 != 0 || a.K < 64 || a.K % 64 != 0 || a.seg_w < 128 ||
         a.seg_w % 128 != 0 || a.N != a.seg_w * a.n_seg || a.n_seg < 1 || a.n_seg > kMaxGemmSeg ||
         a.a_grp < 1 || a.a_stride < 0 || a.a_cols < 64 || a.a_cols % 64 != 0 || a.K % a.a_cols != 0 ||
-        a.a_gstride < 0 || a.o_grp < 1 || a.o_off < 0 || a.o_gstride < 0 || a.act < 0 || a.act > 1)
+        a.a_gstride < 0 || a.o_grp < 1 || a.o_off < 0 || a.o_gstride < 0 || a.act < 0 || a.act > 1 ||
+        a.ksplit < 1 || a.K % (64 * a.ksplit) != 0 || (a.ksplit > 1 && !a.part))
         return hipErrorInvalidValue;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
     // the largest tile that still gives every CU a workgroup
-    const long long t128 = (long long)((a.M + 127) / 128) * (a.N / 128);
-    const long long t64x128 = (long long)((a.M + 63) / 64) * (a.N / 128);
-    const long long t64 = (long long)((a.M + 63) / 64) * (a.N / 64);
-    if (t64 > INT32_MAX) return hipErrorInvalidValue;   // (t128 <= t64x128 <= t64)
+    const long long t128 = (long long)((a.M + 127) / 128) * (a.N / 128) * a.ksplit;
+    const long long t64x128 = (long long)((a.M + 63) / 64) * (a.N / 128) * a.ksplit;
+    const long long t64 = (long long)((a.M + 63) / 64) * (a.N / 64) * a.ksplit;
+    if (t64 > INT32_MAX || (long long)a.M * a.N / 4 > INT32_MAX)
+        return hipErrorInvalidValue;   // (t128 <= t64x128 <= t64)
     if (t128 >= cus)
         hipLaunchKernelGGL(k_gemm<G128>, dim3((unsigned)t128), dim3(256), 0, s, a);
     else if (t64x128 >= cus)
         hipLaunchKernelGGL(k_gemm<G64x128>, dim3((unsigned)t64x128), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(k_gemm<G64>, dim3((unsigned)t64), dim3(256), 0, s, a);
+    if (a.ksplit > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const long long n = (long long)a.M * a.N / 4;
+        hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

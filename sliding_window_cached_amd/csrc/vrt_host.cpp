@@ -926,10 +926,14 @@ int vrt_conv_out_frames(const vrt_conv_stem* c, int n_frames) {
     return conv1_outputs(c->pending + n_frames);
 }
 
+// conv1 runs as kConv1Split k parts (one per tap) and an ordered reduce
+constexpr int kConv1Split = 3;
+
 size_t vrt_conv_workspace_bytes(int n_mel, int d_model, int n_stems, int n_frames) {
     if (!conv_dims_ok(n_mel, d_model) || n_stems < 1 || n_frames < 1) return 0;
     return pad256((size_t)n_stems * (n_frames + kConvPad0) * n_mel * 2) +
-           pad256((size_t)n_stems * (n_frames + 2) * d_model * 2);
+           pad256((size_t)n_stems * (n_frames + 2) * d_model * 2) +
+           (size_t)kConv1Split * n_stems * ((n_frames + 2) / 2) * d_model * 4;   // conv1's fp32 parts
 }
 
 vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const void* mel,
@@ -1016,6 +1020,9 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
         g1.seg_w = d;
         g1.n_seg = 1;
         g1.seg[0] = GemmSeg{out, w->b1, d};
+        // one k part per tap: three times the workgroups of a 3 d-deep product
+        g1.ksplit = kConv1Split;
+        g1.part = (float*)(st1 + pad256((size_t)n_stems * (n_frames + 2) * d * 2));
         if (note(launch_gemm(g1, stream)) != hipSuccess) return VRT_ERR_DEVICE;
     }
     // new caches, in one launch: the last two staged mel rows; the conv0 rows from 2 o on

@@ -170,6 +170,12 @@ struct GemmArgs {
     int o_grp, o_off;
     long long o_gstride;
     int act;            // 0: none; 1: GELU (exact, erf form) after bias and residual
+    // ksplit > 1: the k range is cut into ksplit equal parts (each a multiple
+    // of 64 and of a_cols); workgroup part s writes its fp32 sums to
+    // part[s][m][n], and an ordered reduce then forms the output as above
+    // from ((part 0 + part 1) + part 2) + ...
+    int ksplit;
+    float* part;
 };
 inline void gemm_plain(GemmArgs* g) {
     g->a_grp = g->M;
@@ -180,6 +186,8 @@ inline void gemm_plain(GemmArgs* g) {
     g->o_off = 0;
     g->o_gstride = 0;
     g->act = 0;
+    g->ksplit = 1;
+    g->part = nullptr;
 }
 
 // ---- causal conv stem (vrt_block.hip): row copies between each stem's
