@@ -240,6 +240,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         return;
     }
     const int seg = n0 / a.seg_w;
+    // output group of a row: the fp32 reciprocal gives the quotient within
+    // one, which two compares correct; exact for every row below 2^22
+    // (checked exhaustively), else the integer division
+    const bool fastdiv = a.M <= (1 << 22);
+    const float ogi = 1.0f / (float)a.o_grp;
     char* out = (char*)a.seg[seg].out;
     const char* bias = (const char*)a.seg[seg].bias;
     const long long ldo = a.seg[seg].ld;
@@ -259,7 +264,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
                     v += __uint_as_float(
                         (uint32_t)*(const uint16_t*)((const char*)a.R + ((long long)row * a.ldr + col) * 2) << 16);
                 if (a.act == 1) v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
-                const int og = row / a.o_grp;
+                int og;
+                if (fastdiv) {
+                    og = (int)((float)row * ogi);
+                    og += (og + 1) * a.o_grp <= row;
+                    og -= og * a.o_grp > row;
+                } else {
+                    og = row / a.o_grp;
+                }
                 const long long orow = (long long)og * a.o_gstride + (row - og * a.o_grp) + a.o_off;
                 *(uint16_t*)(out + (orow * ldo + lc) * 2) = to_bf16(v);
             }
