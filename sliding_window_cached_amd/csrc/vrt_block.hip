@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 
     // epilogue: lane l, register r of block (i, j) holds row
     // 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32 of the block
-    if (a.ksplit > 1) {   // fp32 sums of this k part; the reduce finishes them
+    if (a.ksplit > 1) {   // fp32 sums of this k part (128 bytes per half-wave row); the reduce finishes them
         float* pp = a.part + (long long)ks * a.M * a.N;
 #pragma unroll
         for (int j = 0; j < L::JB; ++j) {
@@ -261,42 +261,88 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         }
         return;
     }
+    // The one-pass finish goes through LDS: the waves park their fp32 sums in
+    // a [BM][BN + 8] tile (the pad puts the two half-waves' rows 32 banks
+    // apart), then each thread finishes 4 adjacent columns of a row at a time,
+    // so a row's output offset is worked out once per workgroup and the bias,
+    // residual and output move as 8-byte vectors.
+    constexpr int CS = L::BN + 8;
+    constexpr int CPR = L::BN / 4, RPP = 256 / CPR, NP = L::BM / RPP;   // chunks per row, rows per pass, passes
+    static_assert(L::BM * CS * 4 + L::BM * 8 <= L::BYTES, "staging tile fits the stages");
+    float* C = (float*)lds;
+    long long* orow_l = (long long*)(lds + L::BM * CS * 4);
+    __syncthreads();   // every wave is done with the last stage
+#pragma unroll
+    for (int i = 0; i < L::IB; ++i)
+#pragma unroll
+        for (int j = 0; j < L::JB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                C[((L::BM / 2) * wm + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3)) * CS + (L::BN / 2) * wn + 32 * j +
+                  lr] = acc[i][j][r];
+    const int ch = threadIdx.x % CPR, rr = threadIdx.x / CPR;
+    const int col = n0 + 4 * ch;
+    if (threadIdx.x < L::BM) {   // output row of each product row: (m / o_grp) o_gstride + m % o_grp + o_off
+        const int row = min(m0 + (int)threadIdx.x, a.M - 1);
+        const int og = row / a.o_grp;
+        orow_l[threadIdx.x] = (long long)og * a.o_gstride + (row - og * a.o_grp) + a.o_off;
+    }
+    __syncthreads();
     const int seg = n0 / a.seg_w;
-    // output group of a row: the fp32 reciprocal gives the quotient within
-    // one, which two compares correct; exact for every row below 2^22
-    // (checked exhaustively), else the integer division
-    const bool fastdiv = a.M <= (1 << 22);
-    const float ogi = 1.0f / (float)a.o_grp;
     char* out = (char*)a.seg[seg].out;
     const char* bias = (const char*)a.seg[seg].bias;
     const long long ldo = a.seg[seg].ld;
+    const int lc = col - seg * a.seg_w;
+    // 8-byte moves when every address allows them, else 2-byte ones
+    const bool v8 = (((uintptr_t)out | (uintptr_t)bias | (uintptr_t)a.R | (uintptr_t)(ldo * 2) |
+                      (uintptr_t)(a.ldr * 2)) & 7) == 0;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+        if (v8) {
+            const uint2 b = *(const uint2*)(bias + 2 * lc);
+            bv[0] = bf_lo(b.x); bv[1] = bf_hi(b.x); bv[2] = bf_lo(b.y); bv[3] = bf_hi(b.y);
+        } else {
 #pragma unroll
-    for (int j = 0; j < L::JB; ++j) {
-        const int col = n0 + (L::BN / 2) * wn + 32 * j + lr;
-        const int lc = col - seg * a.seg_w;
-        const float bv = bias ? __uint_as_float((uint32_t)*(const uint16_t*)(bias + 2 * lc) << 16) : 0.f;
+            for (int u = 0; u < 4; ++u) bv[u] = __uint_as_float((uint32_t)*(const uint16_t*)(bias + 2 * (lc + u)) << 16);
+        }
+    }
+    // residual rows first, all in flight together
+    uint2 rv[NP];
 #pragma unroll
-        for (int i = 0; i < L::IB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + (L::BM / 2) * wm + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
-                if (row >= a.M) continue;
-                float v = acc[i][j][r] + bv;
-                if (a.R)
-                    v += __uint_as_float(
-                        (uint32_t)*(const uint16_t*)((const char*)a.R + ((long long)row * a.ldr + col) * 2) << 16);
-                if (a.act == 1) v = gelu_erf(v);
-                int og;
-                if (fastdiv) {
-                    og = (int)((float)row * ogi);
-                    og += (og + 1) * a.o_grp <= row;
-                    og -= og * a.o_grp > row;
-                } else {
-                    og = row / a.o_grp;
-                }
-                const long long orow = (long long)og * a.o_gstride + (row - og * a.o_grp) + a.o_off;
-                *(uint16_t*)(out + (orow * ldo + lc) * 2) = to_bf16(v);
+    for (int p = 0; p < NP; ++p) {
+        rv[p] = make_uint2(0, 0);
+        const int row = m0 + p * RPP + rr;
+        if (a.R && row < a.M) {
+            const char* rp = (const char*)a.R + ((long long)row * a.ldr + col) * 2;
+            if (v8) {
+                rv[p] = *(const uint2*)rp;
+            } else {
+                const uint16_t* h = (const uint16_t*)rp;
+                rv[p] = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
             }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int lrow = p * RPP + rr;
+        if (m0 + lrow >= a.M) continue;
+        const float4 c4 = *(const float4*)(C + lrow * CS + 4 * ch);
+        const float rs[4] = {bf_lo(rv[p].x), bf_hi(rv[p].x), bf_lo(rv[p].y), bf_hi(rv[p].y)};
+        float v[4] = {c4.x + bv[0], c4.y + bv[1], c4.z + bv[2], c4.w + bv[3]};
+        uint16_t y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (a.R) v[u] += rs[u];
+            if (a.act == 1) v[u] = gelu_erf(v[u]);
+            y[u] = to_bf16(v[u]);
+        }
+        char* op = out + (orow_l[lrow] * ldo + lc) * 2;
+        if (v8) {
+            *(uint2*)op = make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ((uint16_t*)op)[u] = y[u];
+        }
     }
 }
 

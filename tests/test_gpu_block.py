@@ -49,15 +49,27 @@ def test_rmsnorm_elementwise():
 
 
 @pytest.mark.parametrize("M,K,N,bias,res", [(1, 64, 128, True, False), (37, 128, 256, False, True),
-                                            (300, 1280, 1280, True, True), (129, 1280, 3840, True, False)])
+                                            (300, 1280, 1280, True, True), (129, 1280, 3840, True, False),
+                                            (4000, 128, 1280, True, True), (4000, 128, 1280, True, "odd")])
 def test_linear_elementwise(M, K, N, bias, res):
+    """res == "odd": out, bias and residual sit one element past an 8-byte
+    boundary (the 2-byte stores and loads of the epilogue)."""
     rng = np.random.default_rng(M + K + N)
     a = synth.round_to(rng.standard_normal((M, K)).astype(np.float32), "bf16")
     w = synth.round_to((rng.standard_normal((N, K)) / K ** 0.5).astype(np.float32), "bf16")
     b = synth.round_to(0.1 * rng.standard_normal(N).astype(np.float32), "bf16") if bias else None
     r = synth.round_to(rng.standard_normal((M, N)).astype(np.float32), "bf16") if res else None
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    vrt.linear(bf(a), M, K, bf(w), N, bf(b) if bias else None, bf(r) if res else None, out, stream())
+    if res == "odd":
+        def odd(t):
+            buf = torch.empty(t.numel() + 1, dtype=torch.bfloat16, device=DEV)
+            buf[1:] = t.reshape(-1)
+            return buf[1:].view(t.shape)
+        out = odd(torch.zeros((M, N), dtype=torch.bfloat16, device=DEV))
+        bd, rd = odd(bf(b)) if bias else None, odd(bf(r))
+    else:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        bd, rd = bf(b) if bias else None, bf(r) if res else None
+    vrt.linear(bf(a), M, K, bf(w), N, bd, rd, out, stream())
     torch.cuda.synchronize()
     ref = block.linear(a, w, b) + (r if res else 0.0)
     S = np.abs(a).astype(np.float64) @ np.abs(w).astype(np.float64).T + (np.abs(b) if bias else 0.0) \
