@@ -641,15 +641,22 @@ def cpu_baseline_conv(steps: int):
                       f"in fp64 numpy on one thread, {el:.1f} s"}
 
 
-KERNEL_SRC = os.path.join(ROOT, "sliding_window_cached_amd", "csrc", "vrt_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_cached_amd", "csrc", f)
+               for f in ("vrt_kernels.hip", "vrt_block.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 MFMA_BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy.txt")
 
 
 def kernels_sha256() -> str:
+    """First 16 hex digits of the sha256 of the kernel sources, in order
+    (vrt_kernels.hip, then vrt_block.hip): a recorded counter value holds
+    only while both are unchanged."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def workload_key(args, name: str) -> str:

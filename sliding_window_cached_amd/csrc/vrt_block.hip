@@ -114,9 +114,8 @@ __device__ __forceinline__ float gelu_erf(float v) {
 // --------------------------------------------------------------- GEMM ----
 // out[m][n] = sum_k A[m][k] W[n][k] (+ bias[n]) (+ R[m][n]), A and W bf16
 // row-major (W has one row per output feature, as a projection matrix).
-// Workgroup tile BM x BN, k step 64; 4 waves in a 2 x 2 grid, wave (wm, wn)
-// owning rows wm BM/2 .. and columns wn BN/2 .. as (BM/64) x (BN/64) blocks of
-// 32 x 32.  With the 32x32x16 operand layouts (A lane l: row l % 32, k
+// Workgroup tile BM x BN, k step 64; WM x WN waves, wave (wm, wn) owning
+// rows wm BM/WM .. and columns wn BN/WN .. as blocks of 32 x 32.  With the 32x32x16 operand layouts (A lane l: row l % 32, k
 // 8 (l / 32) .. +7; B lane l: column l % 32, the same k) both operands are
 // read the same way from row-major tiles: one 16-byte LDS read per lane per
 // block and k16 step.  Tiles go HBM -> LDS by DMA through NST stages (NST - 1
@@ -125,26 +124,30 @@ __device__ __forceinline__ float gelu_erf(float v) {
 // banks.  Rows of A past M are fetched from row M - 1 and never stored.  The
 // k order of every output element is the same for every tile shape, so the
 // shape changes no result.
-template <int BM_, int BN_, int NST_>
+template <int BM_, int BN_, int NST_, int WM_ = 2, int WN_ = 2>
 struct GT {
     static constexpr int BM = BM_, BN = BN_, BK = 64, NST = NST_;
+    static constexpr int WM = WM_, WN = WN_, NW = WM * WN, NT = 64 * NW;   // wave grid, threads
     static constexpr int RB = BK * 2;               // bytes per tile row
     static constexpr int ATILE = BM * RB, WTILE = BN * RB;
     static constexpr int STAGE = ATILE + WTILE;
-    static constexpr int AIPW = ATILE / 1024 / 4;   // DMA instructions per wave per A tile
-    static constexpr int WIPW = WTILE / 1024 / 4;
+    static constexpr int AIPW = ATILE / 1024 / NW;  // DMA instructions per wave per A tile
+    static constexpr int WIPW = WTILE / 1024 / NW;
     static constexpr int LPW = AIPW + WIPW;         // per stage
-    static constexpr int IB = BM / 64, JB = BN / 64;  // 32 x 32 blocks per wave
+    static constexpr int MW = BM / WM, NWD = BN / WN;  // rows and columns per wave
+    static constexpr int IB = MW / 32, JB = NWD / 32;  // 32 x 32 blocks per wave
     static constexpr int BYTES = NST * STAGE;
+    static_assert(AIPW >= 1 && WIPW >= 1 && AIPW * NW * 1024 == ATILE && WIPW * NW * 1024 == WTILE, "DMA split");
+    static_assert(IB >= 1 && JB >= 1 && IB * 32 == MW && JB * 32 == NWD, "wave blocks");
 };
 __device__ __forceinline__ int gsw(int r) { return (r >> 1) & 7; }
 
 template <class L>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(L::NT) void k_gemm(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / L::WN, wn = wave % L::WN;
     const int ntn = a.N / L::BN;
     const int ntiles = (int)(gridDim.x / a.ksplit);
     const int ks = blockIdx.x / ntiles, tile = blockIdx.x - ks * ntiles;   // k part, output tile
@@ -201,12 +204,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int i = 0; i < L::IB; ++i) {
-            const int ra = (L::BM / 2) * wm + 32 * i + lr;
+            const int ra = L::MW * wm + 32 * i + lr;
             aoff[i][s] = ra * L::RB + 16 * ((2 * s + hf) ^ gsw(ra));
         }
 #pragma unroll
         for (int j = 0; j < L::JB; ++j) {
-            const int rw = (L::BN / 2) * wn + 32 * j + lr;
+            const int rw = L::NWD * wn + 32 * j + lr;
             woff[j][s] = L::ATILE + rw * L::RB + 16 * ((2 * s + hf) ^ gsw(rw));
         }
     }
@@ -250,12 +253,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         float* pp = a.part + (long long)ks * a.M * a.N;
 #pragma unroll
         for (int j = 0; j < L::JB; ++j) {
-            const int col = n0 + (L::BN / 2) * wn + 32 * j + lr;
+            const int col = n0 + L::NWD * wn + 32 * j + lr;
 #pragma unroll
             for (int i = 0; i < L::IB; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + (L::BM / 2) * wm + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    const int row = m0 + L::MW * wm + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3);
                     if (row < a.M) pp[(long long)row * a.N + col] = acc[i][j][r];
                 }
         }
@@ -267,7 +270,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     // so a row's output offset is worked out once per workgroup and the bias,
     // residual and output move as 8-byte vectors.
     constexpr int CS = L::BN + 8;
-    constexpr int CPR = L::BN / 4, RPP = 256 / CPR, NP = L::BM / RPP;   // chunks per row, rows per pass, passes
+    constexpr int CPR = L::BN / 4, RPP = L::NT / CPR, NP = L::BM / RPP;   // chunks per row, rows per pass, passes
+    static_assert(NP * RPP == L::BM && L::NT >= L::BM, "finish passes");
     static_assert(L::BM * CS * 4 + L::BM * 8 <= L::BYTES, "staging tile fits the stages");
     float* C = (float*)lds;
     long long* orow_l = (long long*)(lds + L::BM * CS * 4);
@@ -278,8 +282,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         for (int j = 0; j < L::JB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                C[((L::BM / 2) * wm + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3)) * CS + (L::BN / 2) * wn + 32 * j +
-                  lr] = acc[i][j][r];
+                C[(L::MW * wm + 32 * i + 8 * (r >> 2) + 4 * hf + (r & 3)) * CS + L::NWD * wn + 32 * j + lr] =
+                    acc[i][j][r];
     const int ch = threadIdx.x % CPR, rr = threadIdx.x / CPR;
     const int col = n0 + 4 * ch;
     if (threadIdx.x < L::BM) {   // output row of each product row: (m / o_grp) o_gstride + m % o_grp + o_off
@@ -382,13 +386,17 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a) {
     *(uint2*)(out + (orow * a.seg[seg].ld + lc) * 2) = pk;
 }
 
-// Tile shapes, largest first: 128 x 128 with 3 tiles in flight (one
-// workgroup per CU), 64 x 128 and 64 x 64 with 2 and 3 in flight (two per
-// CU).  For few rows the products are bound by the bytes of re-read tiles
-// at the loaded memory latency, not by the matrix cores; smaller tiles fill
-// more CUs.
-using G128 = GT<128, 128, 4>;
-using G64x128 = GT<64, 128, 3>;
+// Tile shapes, largest first.  Workgroups of 8 waves where the tile allows:
+// the rate at which a CU pulls tiles from L2 into LDS grows with the number
+// of waves issuing the loads, and at these sizes that rate, not the matrix
+// cores, sets the time of a k step.
+//   256 x 128, 4 x 2 waves of 64 x 64, 2 tiles in flight, one workgroup per CU
+//   128 x 128, 2 x 4 waves of 64 x 32, 3 in flight, one per CU
+//    64 x 128, 2 x 4 waves of 32 x 32, 2 in flight, two per CU
+//    64 x  64, 2 x 2 waves of 32 x 32, 3 in flight, two per CU
+using G256x128 = GT<256, 128, 3, 4, 2>;
+using G128 = GT<128, 128, 4, 2, 4>;
+using G64x128 = GT<64, 128, 3, 2, 4>;
 using G64 = GT<64, 64, 4>;
 
 // ------------------------------------------------------- conv stem rows ----
@@ -496,18 +504,22 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    // the largest tile that still gives every CU a workgroup
+    // the largest tile whose workgroups cover at least half the CUs (the
+    // 256-row tile only for two full rounds or more)
+    const long long t256 = (long long)((a.M + 255) / 256) * (a.N / 128) * a.ksplit;
     const long long t128 = (long long)((a.M + 127) / 128) * (a.N / 128) * a.ksplit;
     const long long t64x128 = (long long)((a.M + 63) / 64) * (a.N / 128) * a.ksplit;
     const long long t64 = (long long)((a.M + 63) / 64) * (a.N / 64) * a.ksplit;
     if (t64 > INT32_MAX || (long long)a.M * a.N / 4 > INT32_MAX)
-        return hipErrorInvalidValue;   // (t128 <= t64x128 <= t64)
-    if (t128 >= cus)
-        hipLaunchKernelGGL(k_gemm<G128>, dim3((unsigned)t128), dim3(256), 0, s, a);
-    else if (t64x128 >= cus)
-        hipLaunchKernelGGL(k_gemm<G64x128>, dim3((unsigned)t64x128), dim3(256), 0, s, a);
+        return hipErrorInvalidValue;   // (t256 <= t128 <= t64x128 <= t64)
+    if (t256 >= 2LL * cus)
+        hipLaunchKernelGGL(k_gemm<G256x128>, dim3((unsigned)t256), dim3(G256x128::NT), 0, s, a);
+    else if (2 * t128 >= cus)
+        hipLaunchKernelGGL(k_gemm<G128>, dim3((unsigned)t128), dim3(G128::NT), 0, s, a);
+    else if (2 * t64x128 >= cus)
+        hipLaunchKernelGGL(k_gemm<G64x128>, dim3((unsigned)t64x128), dim3(G64x128::NT), 0, s, a);
     else
-        hipLaunchKernelGGL(k_gemm<G64>, dim3((unsigned)t64), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_gemm<G64>, dim3((unsigned)t64), dim3(G64::NT), 0, s, a);
     if (a.ksplit > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

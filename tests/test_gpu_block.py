@@ -50,7 +50,8 @@ def test_rmsnorm_elementwise():
 
 @pytest.mark.parametrize("M,K,N,bias,res", [(1, 64, 128, True, False), (37, 128, 256, False, True),
                                             (300, 1280, 1280, True, True), (129, 1280, 3840, True, False),
-                                            (4000, 128, 1280, True, True), (4000, 128, 1280, True, "odd")])
+                                            (4000, 128, 1280, True, True), (4000, 128, 1280, True, "odd"),
+                                            (20000, 128, 1280, True, True), (1000, 1280, 1280, True, True)])
 def test_linear_elementwise(M, K, N, bias, res):
     """res == "odd": out, bias and residual sit one element past an 8-byte
     boundary (the 2-byte stores and loads of the epilogue)."""

@@ -83,6 +83,27 @@ def test_conv_stem_oracle_and_chunkings():
         assert err <= 1e-2 * mx
 
 
+def test_conv_stem_serving_batch_tile_invariance():
+    """256 stems x 8 mel frames (the serving step: conv0 2048 rows, conv1
+    1024 rows in three k parts, on the large tiles) against the oracle on
+    sampled stems, and bit-identical to the same stems fed as a batch of 3
+    (the smallest tiles): every tile shape keeps each output's k order."""
+    S, T = 256, 8
+    w = synth.conv_weights(74, N_MEL, D)
+    tens, cw = _weights(w)
+    mel_np = np.stack([synth.mel_frames(75, s, T, N_MEL) for s in range(S)])
+    mel = bf(mel_np)
+    say("conv stem: 256 stems, one 8-frame feed")
+    big, _ = _run(S, mel, [T], cw)
+    small, _ = _run(3, mel[:3].contiguous(), [T], cw)
+    assert np.array_equal(big[:3], small)
+    for s in (0, 1, 77, 128, 200, 255):
+        ref = conv.stem(mel_np[s], w)
+        err, mx = float(np.abs(big[s] - ref).max()), float(np.abs(ref).max())
+        say(f"  stream {s}: max abs {err:.3e}, max |ref| {mx:.2f}")
+        assert err <= 1e-2 * mx
+
+
 def test_conv_stem_reset_equals_fresh():
     S, T = 2, 24
     w = synth.conv_weights(72, N_MEL, D)
