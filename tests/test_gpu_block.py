@@ -131,3 +131,28 @@ def test_block_feeds_oracle_and_chunking():
             mx = float(np.abs(ref[ts]).max())
             say(f"  stream {s} {what}: max abs {err:.3e}, max |ref| {mx:.2f}")
             assert err <= 1e-2 * mx
+
+
+def test_block_serving_batch_tile_shapes():
+    """256 streams: a 40-frame feed (the q/k/v product on 256 x 128 tiles,
+    the output product on 128 x 128) then 4-frame feeds (the serving step:
+    128 x 128 and 64 x 128 tiles), bit-identical to the first 3 streams fed
+    as their own batch (64 x 64 tiles throughout), and sampled streams
+    against the fp64 block oracle."""
+    S, T, heads, dim = 256, 48, 20, 1280
+    starts = [(s * 7919) % 1_000_000 for s in range(S)]
+    wts = synth.block_weights(64, 0, dim)
+    xs = [synth.block_input(65, s, 0, T, dim) for s in range(S)]
+    sizes = [40, 4, 4]
+    say("block: 256 streams, feeds of 40, 4, 4")
+    big = _block_run(vrt.ENC_RING, S, T, starts, sizes, wts, xs)
+    say("block: the first 3 streams alone")
+    small = _block_run(vrt.ENC_RING, 3, T, starts[:3], sizes, wts, xs[:3])
+    assert np.array_equal(big[:3], small)
+    ts = [0, 1, 39, 40, 43, 44, 47]
+    for s in (0, 131, 255):
+        ref = block.attn_block(xs[s], wts, heads, starts[s], W, THETA)
+        err = float(np.abs(big[s][ts] - ref[ts]).max())
+        mx = float(np.abs(ref[ts]).max())
+        say(f"  stream {s}: max abs {err:.3e}, max |ref| {mx:.2f}")
+        assert err <= 1e-2 * mx
