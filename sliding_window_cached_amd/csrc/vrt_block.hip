@@ -115,10 +115,10 @@ __device__ __forceinline__ float gelu_erf(float v) {
 // out[m][n] = sum_k A[m][k] W[n][k] (+ bias[n]) (+ R[m][n]), A and W bf16
 // row-major (W has one row per output feature, as a projection matrix).
 // Workgroup tile BM x BN, k step 64; WM x WN waves, wave (wm, wn) owning
-// rows wm BM/WM .. and columns wn BN/WN .. as blocks of 32 x 32.  With the 32x32x16 operand layouts (A lane l: row l % 32, k
-// 8 (l / 32) .. +7; B lane l: column l % 32, the same k) both operands are
-// read the same way from row-major tiles: one 16-byte LDS read per lane per
-// block and k16 step.  Tiles go HBM -> LDS by DMA through NST stages (NST - 1
+// rows wm BM/WM .. and columns wn BN/WN .. as blocks of 32 x 32.  With the
+// 32x32x16 operand layouts (A lane l: row l % 32, k 8 (l / 32) .. +7; B lane
+// l: column l % 32, the same k) both operands are read the same way from
+// row-major tiles: one 16-byte LDS read per lane per block and k16 step.  Tiles go HBM -> LDS by DMA through NST stages (NST - 1
 // in flight while one is read); rows are 128 bytes, their 16-byte chunks
 // XOR-swizzled by (row / 2) mod 8, so the 32 rows read together hit distinct
 // banks.  Rows of A past M are fetched from row M - 1 and never stored.  The
@@ -358,20 +358,30 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a) {
     const int nq = a.N / 4;
     if (x >= (long long)a.M * nq) return;
     const int row = (int)(x / nq), col = (int)(x - (long long)row * nq) * 4;
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
     const long long mn = (long long)a.M * a.N, o = (long long)row * a.N + col;
-    float4 v = *(const float4*)(a.part + o);
+    // the parts are read once: non-temporal loads
+    f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)(a.part + o));
     for (int s = 1; s < a.ksplit; ++s) {
-        const float4 w = *(const float4*)(a.part + s * mn + o);
+        const f32x4_t w = __builtin_nontemporal_load((const f32x4_t*)(a.part + s * mn + o));
         v.x = v.x + w.x; v.y = v.y + w.y; v.z = v.z + w.z; v.w = v.w + w.w;
     }
     const int seg = col / a.seg_w, lc = col - seg * a.seg_w;
     char* out = (char*)a.seg[seg].out;
     const char* bias = (const char*)a.seg[seg].bias;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias && ((uintptr_t)bias & 7) == 0) {   // lc is a multiple of 4
+        const uint2 b = *(const uint2*)(bias + 2 * lc);
+        bv[0] = bf_lo(b.x); bv[1] = bf_hi(b.x); bv[2] = bf_lo(b.y); bv[3] = bf_hi(b.y);
+    } else if (bias) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bv[u] = __uint_as_float((uint32_t)*(const uint16_t*)(bias + 2 * (lc + u)) << 16);
+    }
     float t[4] = {v.x, v.y, v.z, v.w};
     uint16_t y[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        float w = t[u] + (bias ? __uint_as_float((uint32_t)*(const uint16_t*)(bias + 2 * (lc + u)) << 16) : 0.f);
+        float w = t[u] + bv[u];
         if (a.R)
             w += __uint_as_float(
                 (uint32_t)*(const uint16_t*)((const char*)a.R + ((long long)row * a.ldr + col + u) * 2) << 16);
