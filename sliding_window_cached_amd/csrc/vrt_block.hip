@@ -350,10 +350,39 @@ __global__ __launch_bounds__(L::NT) void k_gemm(GemmArgs a) {
     }
 }
 
+// One (segment, group, row) item of a row copy (k_row_copy, and the copy
+// that rides on the split-product reduce): workgroup b of the copy's range.
+__device__ __forceinline__ void row_copy_block(const RowCopyArgs& a, const RowCopyTable& t, int b) {
+    int si = 0;
+    while (si + 1 < a.n_seg && b >= a.n_groups * a.seg[si].rows) {
+        b -= a.n_groups * a.seg[si].rows;
+        ++si;
+    }
+    const RowCopySeg& sg = a.seg[si];
+    const int g = b / sg.rows, r = b - g * sg.rows;
+    char* st = sg.stage + ((long long)g * sg.gstride + sg.off + r) * sg.row_bytes;
+    const char* src = sg.src ? sg.src + ((long long)g * sg.src_gstride + r) * sg.row_bytes
+                             : (const char*)t.cache[g] + sg.cache_off + (long long)r * sg.row_bytes;
+    for (int c = threadIdx.x; c < sg.row_bytes / 16; c += blockDim.x) {
+        if (sg.to_cache) {
+            *(uint4*)((char*)t.cache[g] + sg.cache_off + (long long)r * sg.row_bytes + 16 * c) =
+                *(const uint4*)(st + 16 * c);
+        } else {
+            const uint4 v = (!sg.src && sg.zero_fresh && t.fresh[g]) ? make_uint4(0, 0, 0, 0)
+                                                                    : *(const uint4*)(src + 16 * c);
+            *(uint4*)(st + 16 * c) = v;
+        }
+    }
+}
+
 // Ordered reduce of a split product: one thread per (row, 4 columns); the
 // parts are added in ascending order, then bias, residual and activation as
 // in the one-pass epilogue, rounded once to bf16.
-__global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a) {
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int red_blocks, RowCopyArgs c, RowCopyTable ct) {
+    if ((int)blockIdx.x >= red_blocks) {   // workgroups past the reduce: an independent row copy
+        row_copy_block(c, ct, (int)blockIdx.x - red_blocks);
+        return;
+    }
     const long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const int nq = a.N / 4;
     if (x >= (long long)a.M * nq) return;
@@ -413,28 +442,9 @@ using G64 = GT<64, 64, 4>;
 // One workgroup per (segment, stem, row): 16-byte chunks between a stem's
 // cache rows (or the new input rows) and its staging rows; a fresh stem's
 // cache reads as zeros (the causal left padding).  Segments are laid out one
-// after the other over the grid.
+// after the other over the workgroups.
 __global__ __launch_bounds__(64) void k_row_copy(RowCopyArgs a, RowCopyTable t) {
-    int b = blockIdx.x, si = 0;
-    while (si + 1 < a.n_seg && b >= a.n_groups * a.seg[si].rows) {
-        b -= a.n_groups * a.seg[si].rows;
-        ++si;
-    }
-    const RowCopySeg& sg = a.seg[si];
-    const int g = b / sg.rows, r = b - g * sg.rows;
-    char* st = sg.stage + ((long long)g * sg.gstride + sg.off + r) * sg.row_bytes;
-    const char* src = sg.src ? sg.src + ((long long)g * sg.src_gstride + r) * sg.row_bytes
-                             : (const char*)t.cache[g] + sg.cache_off + (long long)r * sg.row_bytes;
-    for (int c = threadIdx.x; c < sg.row_bytes / 16; c += blockDim.x) {
-        if (sg.to_cache) {
-            *(uint4*)((char*)t.cache[g] + sg.cache_off + (long long)r * sg.row_bytes + 16 * c) =
-                *(const uint4*)(st + 16 * c);
-        } else {
-            const uint4 v = (!sg.src && sg.zero_fresh && t.fresh[g]) ? make_uint4(0, 0, 0, 0)
-                                                                    : *(const uint4*)(src + 16 * c);
-            *(uint4*)(st + 16 * c) = v;
-        }
-    }
+    row_copy_block(a, t, blockIdx.x);
 }
 
 // ------------------------------------------------ read-ceiling probe ----
@@ -481,17 +491,21 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s) {
-    if (a.n_groups < 1 || a.n_groups > kMaxStems || a.n_seg < 1 || a.n_seg > kMaxCopySeg)
-        return hipErrorInvalidValue;
+// workgroups of a row copy, or -1 when its arguments are invalid
+static long long row_copy_blocks(const RowCopyArgs& a) {
+    if (a.n_groups < 1 || a.n_groups > kMaxStems || a.n_seg < 1 || a.n_seg > kMaxCopySeg) return -1;
     long long blocks = 0;
     for (int i = 0; i < a.n_seg; ++i) {
         const RowCopySeg& g = a.seg[i];
-        if (g.rows < 0 || g.row_bytes < 16 || g.row_bytes % 16 || !g.stage || (g.to_cache && g.src))
-            return hipErrorInvalidValue;
+        if (g.rows < 0 || g.row_bytes < 16 || g.row_bytes % 16 || !g.stage || (g.to_cache && g.src)) return -1;
         blocks += (long long)a.n_groups * g.rows;
     }
-    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    return blocks > INT32_MAX ? -1 : blocks;
+}
+
+hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s) {
+    const long long blocks = row_copy_blocks(a);
+    if (blocks < 0) return hipErrorInvalidValue;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(k_row_copy, dim3((unsigned)blocks), dim3(64), 0, s, a, t);
     return hipGetLastError();
@@ -503,7 +517,9 @@ hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowCopyArgs* tail, const RowCopyTable* tail_t) {
+    const long long tail_blocks = tail ? row_copy_blocks(*tail) : 0;
+    if (tail_blocks < 0 || (tail && !tail_t)) return hipErrorInvalidValue;
     if (a.M < 1 || a.N < 128 || a.N % 128 != 0 || a.K < 64 || a.K % 64 != 0 || a.seg_w < 128 ||
         a.seg_w % 128 != 0 || a.N != a.seg_w * a.n_seg || a.n_seg < 1 || a.n_seg > kMaxGemmSeg ||
         a.a_grp < 1 || a.a_stride < 0 || a.a_cols < 64 || a.a_cols % 64 != 0 || a.K % a.a_cols != 0 ||
@@ -533,8 +549,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     if (a.ksplit > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const long long n = (long long)a.M * a.N / 4;
-        hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+        // the reduce's workgroups, then the row copy's (independent of the reduce)
+        const long long n = (long long)a.M * a.N / 4, red = (n + 255) / 256;
+        if (red + tail_blocks > INT32_MAX) return hipErrorInvalidValue;
+        static const RowCopyArgs no_copy{};
+        static const RowCopyTable no_table{};
+        hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)(red + tail_blocks)), dim3(256), 0, s, a, (int)red,
+                           tail ? *tail : no_copy, tail ? *tail_t : no_table);
+    } else if (tail_blocks > 0) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_row_copy(*tail, *tail_t, s);
     }
     return hipGetLastError();
 }

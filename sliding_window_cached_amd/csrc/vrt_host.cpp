@@ -1002,6 +1002,14 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
     g0.n_seg = 1;
     g0.seg[0] = GemmSeg{st1, w->b0, d};
     if (note(launch_gemm(g0, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    // new caches: the last two staged mel rows; the conv0 rows from 2 o on.  They
+    // read only staging rows that conv0 has written, so when conv1 runs they ride
+    // on its reduce launch, else they are one launch of their own.
+    RowCopyArgs cout{};
+    cout.n_groups = n_stems;
+    cout.n_seg = 2;
+    cout.seg[0] = RowCopySeg{kConvPad0, n_mel * 2, 1, st0, n_frames + kConvPad0, n_frames, 0, nullptr, 0, 0};
+    cout.seg[1] = RowCopySeg{keep, d * 2, 1, st1, L, 2LL * o, pend_off, nullptr, 0, 0};
     if (o > 0) {
         GemmArgs g1{};
         g1.A = st1;
@@ -1023,17 +1031,9 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
         // one k part per tap: three times the workgroups of a 3 d-deep product
         g1.ksplit = kConv1Split;
         g1.part = (float*)(st1 + pad256((size_t)n_stems * (n_frames + 2) * d * 2));
-        if (note(launch_gemm(g1, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+        if (note(launch_gemm(g1, stream, &cout, &t)) != hipSuccess) return VRT_ERR_DEVICE;
     }
-    // new caches, in one launch: the last two staged mel rows; the conv0 rows from 2 o on
-    {
-        RowCopyArgs a{};
-        a.n_groups = n_stems;
-        a.n_seg = 2;
-        a.seg[0] = RowCopySeg{kConvPad0, n_mel * 2, 1, st0, n_frames + kConvPad0, n_frames, 0, nullptr, 0, 0};
-        a.seg[1] = RowCopySeg{keep, d * 2, 1, st1, L, 2LL * o, pend_off, nullptr, 0, 0};
-        if (note(launch_row_copy(a, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
-    }
+    if (o == 0 && note(launch_row_copy(cout, t, stream)) != hipSuccess) return VRT_ERR_DEVICE;
     for (int i = 0; i < n_stems; ++i) {
         stems[i]->pending = keep;
         stems[i]->fresh = false;

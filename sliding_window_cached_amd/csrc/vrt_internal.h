@@ -215,10 +215,15 @@ struct RowCopyTable {
     int fresh[kMaxStems];
 };
 hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStream_t s);
+// A product; with ksplit > 1 the ordered reduce follows, and `tail` (with its
+// table), an independent row copy, rides on the reduce launch as extra
+// workgroups; with ksplit = 1 it is launched after the product.
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowCopyArgs* tail = nullptr,
+                       const RowCopyTable* tail_t = nullptr);
 hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
 
 hipError_t launch_rope_append(const AppendArgs& a, const StateTable& t, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t s);
