@@ -60,45 +60,102 @@ def log(*a):
 
 
 def attn_work(n_kv: int, n: int, elem: int = 2):
-    """Algorithmic bytes and flops of one unit's attention over a sub-batch of
-    n frames when the ring held n_kv rows before it: read the n new queries,
-    the keys and values of the union window (min(n_kv, W-1) old rows plus the
-    n new ones), write n outputs; 4*d flops per (query, visible key) per head."""
+    """Algorithmic bytes and flops of one unit-step of the path (RoPE, append
+    and attention) over a sub-batch of n frames when the ring held n_kv rows
+    before it, in its fused minimum: read the n new q, k and v rows, write the
+    n rotated-key and value rows into the ring, read the keys and values of
+    the min(n_kv, W-1) older rows of the window, write n outputs:
+    (3n + 2n + 2 old + n) R e bytes; 4 d flops per (query, visible key) per
+    head."""
     old = min(n_kv, W - 1)
-    nbytes = (n + 2 * (old + n) + n) * R * elem
+    nbytes = (6 * n + 2 * old) * R * elem
     visible = sum(min(W, n_kv + j + 1) for j in range(n))
     return nbytes, 4 * D * H * visible
 
 
-def cpu_baseline(streams: int, layers_in_config: int, pre: int, steps: int, n: int, scale: float,
-                 starts, what: str):
-    """The fp64 oracle (streamed form, the method itself) on a bounded sample:
-    `streams` single-layer streams pre-filled with `pre` frames (not timed),
-    then `steps` feeds of `n` frames (timed).  The rate is divided by the
-    configuration's layer count, so it is in the same unit as the GPU value
-    (frames through every layer)."""
+def attn_kernel_bytes(n_kv: int, n: int, elem: int = 2) -> int:
+    """Bytes the matrix-path attention kernel itself must move for one unit
+    (its rows were appended by a separate launch): the n queries, the keys
+    and values of the whole window (old rows and the n new ones), n outputs."""
+    old = min(n_kv, W - 1)
+    return (n + 2 * (old + n) + n) * R * elem
+
+
+def compaction_bytes(units: int, elem: int = 2) -> int:
+    """One compaction per unit: the last W rows of K and V read and written."""
+    return units * 2 * 2 * W * R * elem
+
+
+def oracle_stream_run(job):
+    """One single-layer stream of the fp64 oracle (streamed form): pre-filled
+    with `pre` frames (not timed), then `steps` feeds of `n` frames, timed.
+    Returns (start, end) of the timed feeds on the system-wide monotonic
+    clock.  Runs in the calling process on one BLAS thread."""
+    from threadpoolctl import threadpool_limits
     from oracle.stream import EncStream
     from synth import qkv
 
-    T = pre + steps * n
-    elapsed = 0.0
-    for s in range(streams):
-        q, k, v = qkv(2, s, 0, T, H, H, D, scale, "bf16")
-        st = EncStream(H, D, start_pos=int(starts[s]))
+    seed, s, start, pre, steps, n, scale = job
+    with threadpool_limits(limits=1):
+        T = pre + steps * n
+        q, k, v = qkv(seed, s, 0, T, H, H, D, scale, "bf16")
+        st = EncStream(H, D, start_pos=int(start))
         if pre:
             st.feed(q[:pre], k[:pre], v[:pre])
         t0 = time.perf_counter()
         for i in range(steps):
             a = pre + i * n
             st.feed(q[a:a + n], k[a:a + n], v[a:a + n])
-        elapsed += time.perf_counter() - t0
-    frame_layers = streams * steps * n
-    return {"value": frame_layers / elapsed / layers_in_config, "unit": "frames/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{what}: {streams} stream(s) x 1 layer x {steps} feeds of {n} frames "
-                      f"(rings pre-filled with {pre} frames, not timed), oracle.stream.EncStream "
-                      f"in fp64 numpy on one thread, {elapsed:.1f} s for {frame_layers} "
-                      f"frame-layers, divided by {layers_in_config} layer(s) per frame"}
+        return t0, time.perf_counter()
+
+
+CPU_POOL = None
+
+
+def start_cpu_pool():
+    """Worker processes for the all-core oracle baseline, started before
+    anything touches the GPU (each is a fresh interpreter; nothing is forked
+    from a process that holds the GPU).  One per host core of this job's
+    share, at most 16."""
+    global CPU_POOL
+    import multiprocessing as mp
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    CPU_POOL = (mp.get_context("spawn").Pool(n), n)
+
+
+def cpu_baseline(layers_in_config: int, pre: int, steps: int, n: int, scale: float, starts, what: str,
+                 seed: int, steps_1t: int = None):
+    """The fp64 oracle (streamed form, the method itself) on a bounded sample
+    of the workload: single-layer streams pre-filled with `pre` frames (not
+    timed), then `steps` feeds of `n` frames (timed).  All cores: one stream
+    per worker process, all at once, the rate taken over the span from the
+    first worker's start to the last one's end.  One thread: one stream in
+    this process.  Rates are divided by the configuration's layer count, so
+    they are in the same unit as the GPU value (frames through every layer)."""
+    steps_1t = steps if steps_1t is None else steps_1t
+    t0, t1 = oracle_stream_run((seed, 0, int(starts[0]), pre, steps_1t, n, scale))
+    one = {"value": steps_1t * n / (t1 - t0) / layers_in_config, "threads": 1,
+           "sample": f"1 stream x 1 layer x {steps_1t} feeds of {n} frames, {t1 - t0:.1f} s"}
+    res = {"value": one["value"], "unit": "frames/s", "cores": 1, "kind": "oracle",
+           "host_cpu_count": os.cpu_count(), "single_thread": one}
+    if CPU_POOL is not None:
+        pool, nproc = CPU_POOL
+        jobs = [(seed, s, int(starts[s % len(starts)]), pre, steps, n, scale) for s in range(nproc)]
+        spans = pool.map_async(oracle_stream_run, jobs).get(timeout=600)
+        span = max(b for _, b in spans) - min(a for a, _ in spans)
+        res["value"] = nproc * steps * n / span / layers_in_config
+        res["cores"] = nproc
+        res["sample"] = (f"{what}: {nproc} streams x 1 layer x {steps} feeds of {n} frames, one stream "
+                         f"per worker process on {nproc} host cores at once (rings pre-filled with {pre} "
+                         f"frames, not timed), oracle.stream.EncStream in fp64 numpy, one BLAS thread "
+                         f"each, {span:.1f} s from the first start to the last end for {nproc * steps * n} "
+                         f"frame-layers, divided by {layers_in_config} layer(s) per frame; "
+                         f"single_thread: the same on one stream in one thread")
+    else:
+        res["sample"] = (f"{what}: " + one["sample"] + f" (rings pre-filled with {pre} frames, not timed), "
+                         f"oracle.stream.EncStream in fp64 numpy on one thread, divided by "
+                         f"{layers_in_config} layer(s) per frame")
+    return res
 
 
 def cpu_baseline_block(steps: int):
@@ -237,7 +294,7 @@ def bench_c2(args):
         nkv_seen.append(nkv_after - n)
         nkv = nkv_after
 
-    every = max(1, args.timing_every)
+    every = max(1, args.timing_every or (1 if args.steps < 100 else 10))
     timed = list(range(0, args.steps, every))
     ev = dict(zip(timed, _timing_events(len(timed))))
     log(f"c2: timing {args.steps} steps (attention events on every {every})")
@@ -254,6 +311,31 @@ def bench_c2(args):
     wall = time.perf_counter() - t0
     vrt.set_attn_events()
     attn_ms = [ev[j][0].elapsed_time(ev[j][1]) for j in timed]
+    srt = sorted(attn_ms)
+    log(f"c2: attention launches (us): min {srt[0] * 1e3:.1f}, median {srt[len(srt) // 2] * 1e3:.1f}, "
+        f"max {srt[-1] * 1e3:.1f}; first {attn_ms[0] * 1e3:.1f}")
+
+    # one compaction of all 256 rings (every 196 steps in steady state: the
+    # ring goes from 754 to 1536 rows 4 at a time), timed on its own after
+    # the timed steps, with events on the launch stream
+    comp_every = (desc.ring_slots - W) // n if desc.kind == vrt.ENC_RING else None
+    comp = None
+    if comp_every:
+        cev = _timing_events(3)
+        comp_ms = []
+        for a, b in cev:
+            vrt.enc_attn_feed(states, 0, 1, Q[-1], K[-1], V[-1], n, out, stream)   # n_kv > W again
+            a.record()
+            vrt.ring_compact(states, 0, 1, stream)
+            b.record()
+        torch.cuda.synchronize()
+        comp_ms = sorted(a.elapsed_time(b) for a, b in cev)
+        cb = compaction_bytes(S)
+        c_us = comp_ms[1] * 1e3
+        comp = {"launch_us": c_us, "bytes": cb, "achieved_gbs": cb / (c_us * 1e-6) / 1e9,
+                "every_steps": comp_every,
+                "note": "k_compact over all 256 rings, median of 3 launches timed with events after "
+                        "the timed steps; in steady state one step in every_steps carries it"}
     for s in states:
         s.close()
 
@@ -261,6 +343,12 @@ def bench_c2(args):
     nbytes = [S * attn_work(nkv_seen[j], n)[0] for j in timed]   # the sampled launches
     t_kernel = sum(attn_ms) * 1e-3 / len(attn_ms)
     achieved = sum(nbytes) / (sum(attn_ms) * 1e-3) / 1e9
+    if comp:
+        step_s = wall / args.steps
+        comp["value_amortized"] = S * n / (step_s + comp["launch_us"] * 1e-6 / comp_every)
+        comp["roofline_frac_amortized"] = (
+            (nbytes[-1] + comp["bytes"] / comp_every) / (t_kernel + comp["launch_us"] * 1e-6 / comp_every)
+            / 1e9 / HBM_PEAK_GBS)
     return {
         "metric": METRIC,
         "value": frames / wall,
@@ -291,10 +379,14 @@ def bench_c2(args):
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": (measured_traffic("k_attn", workload_key(args, "c2")) or {}).get("bytes"),
             "alg_bytes_per_launch": nbytes[-1],
+            "bytes_model": "(3n + 2n + 2 old + n) * 1280 * 2 B per stream: n = 4 new q, k, v rows "
+                           "read, their K/V rows written, old = 749 window rows of K and V read, n "
+                           "outputs written",
             "launch_us_mean": t_kernel * 1e6,
             "launches_timed": len(attn_ms),
         },
         "compaction_steps": sum(compacting),
+        "compaction": comp,
         "step_hbm_frac": sum(S * attn_work(k, n)[0] for k in nkv_seen) / wall / 1e9 / HBM_PEAK_GBS,
     }
 
@@ -347,7 +439,7 @@ def bench_c2b(args):
         nkv_seen.append(nkv_after - n)
         nkv = nkv_after
 
-    every = max(1, args.timing_every)
+    every = max(1, args.timing_every or (1 if args.steps < 100 else 10))
     timed = list(range(0, args.steps, every))
     ev = dict(zip(timed, _timing_events(len(timed))))
     blk = dict(zip(timed, _timing_events(len(timed))))
@@ -447,7 +539,7 @@ def bench_cs(args):
     for i in range(args.warmup):
         vrt.conv_stem_feed(stems, mel[i], n, cw, out, ws, wsb, stream)
     torch.cuda.synchronize()
-    every = max(1, args.timing_every)
+    every = max(1, args.timing_every or (1 if args.steps < 100 else 10))
     timed = list(range(0, args.steps, every))
     ev = dict(zip(timed, _timing_events(len(timed))))
     log(f"cs: timing {args.steps} conv stem steps")
@@ -534,7 +626,7 @@ def bench_cm(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    every = max(1, args.timing_every)
+    every = max(1, args.timing_every or (1 if args.steps < 100 else 10))
     timed = list(range(0, args.steps, every))
     ev = dict(zip(timed, _timing_events(len(timed))))
     log(f"cm: timing {args.steps} steps of 6 lookahead layers")
@@ -804,6 +896,22 @@ def bench_c1(args):
     wall = time.perf_counter() - t0
     vrt.set_attn_events()
     attn_ms = [a.elapsed_time(b) for a, b in ev]
+
+    # the same kind of step as 32 per-layer calls of 64 streams each (the
+    # order in which a real encoder runs its layers: one layer's output is the
+    # next one's input), on the wall clock, continuing the same streams
+    nl_steps = min(args.steps, 50)
+    Qp, Kp, Vp = (x[args.warmup:args.warmup + nl_steps].transpose(1, 2).contiguous() for x in (Q, K, V))
+    out_l = torch.empty((S, 1, n, H, D), dtype=torch.bfloat16, device=dev)
+    log(f"c1: timing {nl_steps} steps as {L} per-layer calls each")
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for j in range(nl_steps):
+        for l in range(L):
+            vrt.enc_attn_feed(states, l, 1, Qp[j, l], Kp[j, l], Vp[j, l], n, out_l, stream)
+    torch.cuda.synchronize()
+    wall_l = time.perf_counter() - t1
+    del Qp, Kp, Vp
     for st in states:
         st.close()
     nbytes = [L * sum(attn_work(k, n)[0] for k, _ in step) for step in plan]
@@ -843,6 +951,12 @@ def bench_c1(args):
             "launches_timed": len(attn_ms),
         },
         "step_hbm_frac": sum(nbytes) / wall / 1e9 / HBM_PEAK_GBS,
+        "per_layer_calls": {
+            "steps": nl_steps, "ms_per_step": wall_l * 1e3 / nl_steps,
+            "value": S * n * nl_steps / wall_l,
+            "note": "each step as 32 calls (one layer of all 64 streams each, 64 units per launch), "
+                    "wall clock",
+        },
     }
 
 
@@ -935,7 +1049,7 @@ def bench_c3(args):
     frames = sum(m for _, m, _, _ in plan)
     work = [attn_work(k, m) for _, m, k, _ in plan]
     band = [mfma_band(base, base + k, m) for _, m, k, base in plan]
-    nbytes = sum(L * w[0] for w in work)
+    nbytes = sum(L * attn_kernel_bytes(k, m) for _, m, k, _ in plan)
     flops = sum(L * w[1] for w in work)
     t_attn = sum(attn_ms) * 1e-3
     tflops = flops / t_attn / 1e12
@@ -1119,14 +1233,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ring", default="compact", choices=["compact", "mod"],
                     help="encoder configs: compacting ring (the pages') or modulo ring")
-    ap.add_argument("--timing-every", type=int, default=10,
-                    help="c2: record the attention-kernel events on every N-th timed step")
+    ap.add_argument("--timing-every", type=int, default=None,
+                    help="c2: record the attention-kernel events on every N-th timed step "
+                         "(default: every step below 100 steps, else every 10th)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only (--gpus 1): streams are independent and would "
               "shard across GPUs with no exchange; a single GPU is run and reported.",
               file=sys.stderr)
         sys.exit(2)
+    if not args.no_cpu_baseline and args.config in ("c1", "c2", "c3"):
+        start_cpu_pool()    # before anything touches the GPU
     if args.config == "copy":
         args.steps = 20 if args.steps is None else args.steps
         args.warmup = 2 if args.warmup is None else args.warmup
@@ -1171,8 +1288,8 @@ def main():
         log("cpu baseline: timing the fp64 oracle on a bounded sample")
         from synth import offsets
         if args.config == "c2":
-            res["cpu_baseline"] = cpu_baseline(1, 1, W, 1000, 4, 0.5, offsets(2, 1, 10 ** 4, 10 ** 6),
-                                               "steady-state sample")
+            res["cpu_baseline"] = cpu_baseline(1, W, 1000, 4, 0.5, offsets(2, 16, 10 ** 4, 10 ** 6),
+                                               "steady-state sample", seed=2)
         elif args.config == "c2b":
             res["cpu_baseline"] = cpu_baseline_block(750)
         elif args.config == "cs":
@@ -1180,11 +1297,13 @@ def main():
         elif args.config == "cm":
             res["cpu_baseline"] = cpu_baseline_cm(10000, passes=8)
         elif args.config == "c1":
-            res["cpu_baseline"] = cpu_baseline(1, 32, W, 1000, 4, 0.5, [0], "staggered-streams sample")
+            res["cpu_baseline"] = cpu_baseline(32, W, 1000, 4, 0.5, [0], "staggered-streams sample", seed=1)
         elif args.config == "c3":
-            res["cpu_baseline"] = cpu_baseline(1, 32, 0, 10, 512, 1.0, [0], "catch-up sample")
+            res["cpu_baseline"] = cpu_baseline(32, 0, 10, 512, 1.0, [0], "catch-up sample", seed=3)
         else:
             res["cpu_baseline"] = cpu_baseline_dec(res["config"]["contexts"])
+    if CPU_POOL is not None:
+        CPU_POOL[0].terminate()
     print(json.dumps(res), flush=True)
 
 

@@ -26,9 +26,11 @@
  * Conventions for every entry point
  * ---------------------------------
  * - All device pointers are caller-owned; the library never allocates or
- *   frees device memory and holds no global state (apart from the optional
- *   per-thread timing events of vrt_set_attn_events).  All device work is
- *   enqueued on the caller's `stream` and is asynchronous.
+ *   frees device memory and holds no state between calls apart from the
+ *   optional per-thread timing events of vrt_set_attn_events, the testing
+ *   hook of vrt_test_launch_hook, and each device's compute-unit count and
+ *   LDS size, read once.  All device work is enqueued on the caller's
+ *   `stream` and is asynchronous.
  * - Arguments are checked before anything is enqueued.  On any error nothing
  *   is enqueued and no state changes (streaming-plan page, "Per-hook
  *   behavior": validate is pure).
@@ -193,6 +195,19 @@ vrt_status vrt_ring_advance(const vrt_cache_desc* desc, int64_t* abs_base, int32
  * agree within bf16 rounding. */
 int vrt_attn_path(const vrt_cache_desc* desc, int n);
 
+/* Launch plan of the attention kernel for one sub-batch of n frames (for a
+ * decoder desc: n tokens, 1 = the split decode step) over `units`
+ * (state, layer) caches in one launch: the kv heads each workgroup streams
+ * (*heads_per_group), the key splits per (unit, head group) (*n_splits, 1
+ * except for the decode step) and the query chunks per unit (*n_qchunks).
+ * The plan follows the unit count and the current device's compute units
+ * and LDS size (256 and 160 KB when no device answers); outputs are
+ * bit-identical under every plan, since each query's arithmetic depends
+ * only on its own window and the absolute tile grid.  Host-only.
+ * VRT_ERR_INVALID on null outputs, units < 1 or n < 1. */
+vrt_status vrt_attn_plan(const vrt_cache_desc* desc, int64_t units, int n, int32_t* heads_per_group,
+                         int32_t* n_splits, int32_t* n_qchunks);
+
 /* Outputs a feed of n_new frames produces per (state, layer) when that layer
  * has been fed n_kv frames before: n_new for ENC_RING and ENC_MODRING;
  * max(0, n_kv + n_new - F) - max(0, n_kv - F) for ENC_LOOKAHEAD (a query is
@@ -301,13 +316,16 @@ size_t vrt_block_workspace_bytes(const vrt_cache_desc* desc, int n_rows);
  *   y = RMSNorm(x); q = y Wq^T + b_q; k = y Wk^T; v = y Wv^T + b_v;
  *   a = the cached path (vrt_enc_attn_feed with q, k, v, one layer);
  *   out = x + a Wo^T + b_o.
- * x/out: [n_states][n_new][dim].  Encoder states (either ring kind) with
- * bf16 storage and n_heads_q == n_heads_kv; dim a multiple of 128 and at
- * most 2048.  Every check of vrt_enc_attn_feed is made before anything is
- * enqueued, plus VRT_ERR_INVALID for null or misaligned (16-byte) pointers,
- * a nonzero reserved field or eps < 0, VRT_ERR_CAPACITY for a short
- * workspace, VRT_ERR_UNSUPPORTED for other storage or head layouts.
- * The states advance exactly as under vrt_enc_attn_feed. */
+ * x/out: [n_states][n_new][dim].  Encoder ring states (ENC_RING or
+ * ENC_MODRING) with bf16 storage and n_heads_q == n_heads_kv; dim a multiple
+ * of 128 and at most 2048.  ENC_LOOKAHEAD states are refused
+ * (VRT_ERR_UNSUPPORTED): their answered queries lag the rows fed, so the
+ * residual rows would not line up.  Every check of vrt_enc_attn_feed is made
+ * before anything is enqueued, plus VRT_ERR_INVALID for null or misaligned
+ * (16-byte) pointers, a nonzero reserved field or eps < 0, VRT_ERR_CAPACITY
+ * for a short workspace, VRT_ERR_UNSUPPORTED for other storage or head
+ * layouts.  The states advance exactly as under vrt_enc_attn_feed; a failed
+ * launch at any point poisons them. */
 vrt_status vrt_enc_block_feed(vrt_stream_state* const* states, int n_states, int layer,
                               const void* x, int n_new, const vrt_block_weights* w, void* out,
                               void* workspace, size_t ws_bytes, hipStream_t stream);
@@ -361,7 +379,9 @@ size_t vrt_conv_workspace_bytes(int n_mel, int d_model, int n_stems, int n_frame
  * stems must have the same dimensions and the same pending count, and be
  * distinct (VRT_ERR_INVALID otherwise); at most 256 per call.  mel, out,
  * workspace, w0 and w1 16-byte aligned.  The caches advance as the work is
- * enqueued. */
+ * enqueued.  On VRT_ERR_DEVICE the stems are left as they were (host state
+ * and caches): the caches are written only by the call's last launch, so
+ * the feed can be made again. */
 vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const void* mel,
                               int n_frames, const vrt_conv_weights* w, void* out, int32_t* n_out,
                               void* workspace, size_t ws_bytes, hipStream_t stream);
@@ -386,6 +406,22 @@ vrt_status vrt_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t
  * setting the library keeps.  VRT_ERR_INVALID if exactly one is null or a
  * handle is not a valid event. */
 vrt_status vrt_set_attn_events(hipEvent_t start, hipEvent_t stop);
+
+/* Testing only: exercises the error paths and the host planning without
+ * faulting a GPU.  From this call on, on the calling thread, the fail_at-th
+ * kernel launch the library makes (counting from 1; 0 = none) reports a
+ * launch error without launching anything, as a failed launch would; with
+ * dry_run = 1 no kernel is launched at all (every other launch is skipped
+ * and reported successful, and no HIP call is made to enqueue work), so the
+ * metadata, poisoning and "nothing enqueued" rules can be checked on a host
+ * without a GPU.  Device memory is never touched in dry-run mode, but the
+ * state metadata advances as if the work had run.  Setting the hook restarts
+ * the launch count; vrt_test_launch_hook(0, 0) turns it off.
+ * vrt_test_launch_count returns the launches (made, failed or skipped) that
+ * reached the library's launch gate on this thread since the hook was last
+ * set. */
+void vrt_test_launch_hook(int32_t fail_at, int32_t dry_run);
+int64_t vrt_test_launch_count(void);
 
 #ifdef __cplusplus
 }

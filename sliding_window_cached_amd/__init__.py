@@ -33,7 +33,8 @@ EXPORTS = (
     "vrt_rmsnorm", "vrt_linear", "vrt_block_workspace_bytes", "vrt_enc_block_feed",
     "vrt_conv_stem_device_bytes", "vrt_conv_stem_create", "vrt_conv_stem_reset",
     "vrt_conv_stem_destroy", "vrt_conv_stem_query", "vrt_conv_out_frames",
-    "vrt_conv_workspace_bytes", "vrt_conv_stem_feed", "vrt_read_probe",
+    "vrt_conv_workspace_bytes", "vrt_conv_stem_feed", "vrt_read_probe", "vrt_attn_plan",
+    "vrt_test_launch_hook", "vrt_test_launch_count",
 )
 
 
@@ -166,6 +167,10 @@ def _load():
         "vrt_conv_out_frames": (c_int, [P, c_int]),
         "vrt_conv_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
         "vrt_read_probe": (c_int, [P, c_size_t, P, P]),
+        "vrt_attn_plan": (c_int, [POINTER(CacheDesc), c_int64, c_int, POINTER(c_int32),
+                                  POINTER(c_int32), POINTER(c_int32)]),
+        "vrt_test_launch_hook": (None, [c_int32, c_int32]),
+        "vrt_test_launch_count": (c_int64, []),
         "vrt_conv_stem_feed": (c_int, [POINTER(P), c_int, P, c_int, POINTER(ConvWeights), P,
                                        POINTER(c_int32), P, c_size_t, P]),
     }
@@ -224,6 +229,24 @@ def attn_path(desc: CacheDesc, n: int) -> int:
     return lib.vrt_attn_path(byref(desc), n)
 
 
+def attn_plan(desc: CacheDesc, units: int, n: int):
+    """(kv heads per workgroup, key splits, query chunks per unit) of the
+    attention launch for a sub-batch of n frames over `units` caches."""
+    hg, sp, qc = c_int32(), c_int32(), c_int32()
+    _check(lib.vrt_attn_plan(byref(desc), units, n, byref(hg), byref(sp), byref(qc)), "attn_plan")
+    return hg.value, sp.value, qc.value
+
+
+def test_launch_hook(fail_at: int = 0, dry_run: bool = False) -> None:
+    """Testing only: make the fail_at-th next launch fail (0: none); with
+    dry_run, skip every launch (host logic without a GPU)."""
+    lib.vrt_test_launch_hook(fail_at, 1 if dry_run else 0)
+
+
+def test_launch_count() -> int:
+    return lib.vrt_test_launch_count()
+
+
 def ring_advance(desc: CacheDesc, abs_base: int, n_kv: int, n_new: int):
     """Pure host planning of one encoder feed: (abs_base, n_kv, n_compactions)."""
     b, k, c = c_int64(abs_base), c_int32(n_kv), c_int32(0)
@@ -251,6 +274,10 @@ class StreamState:
         if s not in (OK, ERR_POISONED):
             _check(s, "stream_state_query")
         return b.value, k.value
+
+    def status(self) -> int:
+        """OK, or ERR_POISONED after a failed launch (until reset)."""
+        return lib.vrt_stream_state_query(self.handle, 0, None, None)
 
     def close(self) -> None:
         if self.handle:
@@ -288,8 +315,11 @@ def enc_attn_feed(states, layer0, n_layers, q, k, v, n_new, out, stream=0, check
 
 
 def ring_compact(states, layer0, n_layers, stream=0):
-    _check(lib.vrt_ring_compact(_handles(states), len(states), layer0, n_layers, stream),
-           "ring_compact")
+    _check(ring_compact_status(states, layer0, n_layers, stream), "ring_compact")
+
+
+def ring_compact_status(states, layer0, n_layers, stream=0) -> int:
+    return lib.vrt_ring_compact(_handles(states), len(states), layer0, n_layers, stream)
 
 
 def dec_workspace_bytes(desc, n_states, n_layers, n_tok) -> int:

@@ -486,9 +486,9 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p,
 }  // namespace
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, hipStream_t s) {
-    hipLaunchKernelGGL(k_read_probe, dim3(16384), dim3(256), 0, s, (const uint4*)buf,
+    VRT_LAUNCH(k_read_probe, dim3(16384), dim3(256), 0, s, (const uint4*)buf,
                        (long long)(bytes / 16), 0x9e3779b9u, sink);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 // workgroups of a row copy, or -1 when its arguments are invalid
@@ -507,14 +507,14 @@ hipError_t launch_row_copy(const RowCopyArgs& a, const RowCopyTable& t, hipStrea
     const long long blocks = row_copy_blocks(a);
     if (blocks < 0) return hipErrorInvalidValue;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_row_copy, dim3((unsigned)blocks), dim3(64), 0, s, a, t);
-    return hipGetLastError();
+    VRT_LAUNCH(k_row_copy, dim3((unsigned)blocks), dim3(64), 0, s, a, t);
+    return hipSuccess;
 }
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s) {
     if (a.rows < 1 || a.dim < 8 || a.dim % 8 != 0 || a.dim > 2048) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)a.rows), dim3(256), 0, s, a);
-    return hipGetLastError();
+    VRT_LAUNCH(k_rmsnorm, dim3((unsigned)a.rows), dim3(256), 0, s, a);
+    return hipSuccess;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowCopyArgs* tail, const RowCopyTable* tail_t) {
@@ -526,10 +526,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowCopyArgs* tail
         a.a_gstride < 0 || a.o_grp < 1 || a.o_off < 0 || a.o_gstride < 0 || a.act < 0 || a.act > 1 ||
         a.ksplit < 1 || a.K % (64 * a.ksplit) != 0 || (a.ksplit > 1 && !a.part))
         return hipErrorInvalidValue;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
+    const int cus = device_cus();
     // the largest tile whose workgroups cover at least half the CUs (the
     // 256-row tile only for two full rounds or more)
     const long long t256 = (long long)((a.M + 255) / 256) * (a.N / 128) * a.ksplit;
@@ -539,29 +536,25 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowCopyArgs* tail
     if (t64 > INT32_MAX || (long long)a.M * a.N / 4 > INT32_MAX)
         return hipErrorInvalidValue;   // (t256 <= t128 <= t64x128 <= t64)
     if (t256 >= 2LL * cus)
-        hipLaunchKernelGGL(k_gemm<G256x128>, dim3((unsigned)t256), dim3(G256x128::NT), 0, s, a);
+        VRT_LAUNCH(k_gemm<G256x128>, dim3((unsigned)t256), dim3(G256x128::NT), 0, s, a);
     else if (2 * t128 >= cus)
-        hipLaunchKernelGGL(k_gemm<G128>, dim3((unsigned)t128), dim3(G128::NT), 0, s, a);
+        VRT_LAUNCH(k_gemm<G128>, dim3((unsigned)t128), dim3(G128::NT), 0, s, a);
     else if (2 * t64x128 >= cus)
-        hipLaunchKernelGGL(k_gemm<G64x128>, dim3((unsigned)t64x128), dim3(G64x128::NT), 0, s, a);
+        VRT_LAUNCH(k_gemm<G64x128>, dim3((unsigned)t64x128), dim3(G64x128::NT), 0, s, a);
     else
-        hipLaunchKernelGGL(k_gemm<G64>, dim3((unsigned)t64), dim3(G64::NT), 0, s, a);
+        VRT_LAUNCH(k_gemm<G64>, dim3((unsigned)t64), dim3(G64::NT), 0, s, a);
     if (a.ksplit > 1) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         // the reduce's workgroups, then the row copy's (independent of the reduce)
         const long long n = (long long)a.M * a.N / 4, red = (n + 255) / 256;
         if (red + tail_blocks > INT32_MAX) return hipErrorInvalidValue;
         static const RowCopyArgs no_copy{};
         static const RowCopyTable no_table{};
-        hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)(red + tail_blocks)), dim3(256), 0, s, a, (int)red,
+        VRT_LAUNCH(k_gemm_reduce, dim3((unsigned)(red + tail_blocks)), dim3(256), 0, s, a, (int)red,
                            tail ? *tail : no_copy, tail ? *tail_t : no_table);
     } else if (tail_blocks > 0) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         return launch_row_copy(*tail, *tail_t, s);
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace vrt

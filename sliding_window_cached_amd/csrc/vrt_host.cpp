@@ -3,6 +3,7 @@
 // enqueued after every check has passed; the mirrors advance as it is
 // enqueued, so no call ever reads anything back from the GPU.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdio>
@@ -21,6 +22,71 @@ struct vrt_stream_state {
     std::vector<int32_t> n_kv;      // per layer: rows held (decoder: tokens written)
     bool poisoned;
 };
+
+namespace {
+
+// Testing hook (vrt_test_launch_hook): the launch that fails (1-based count
+// since the hook was set; 0 none), whether launches are skipped (dry run),
+// and the launches that reached the gate since the hook was last set.
+thread_local int32_t g_fail_at = 0;
+thread_local int32_t g_dry = 0;
+thread_local int64_t g_launches = 0;
+
+// Compute units and LDS bytes per CU of each device, read once.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+std::atomic<int> g_lds[kMaxDevices];
+
+void device_props(int* cus, int* lds) {
+    *cus = 256;
+    *lds = 160 * 1024;
+    int dev = 0;
+    if (g_dry || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
+    int c = g_cus[dev].load(std::memory_order_relaxed), l = g_lds[dev].load(std::memory_order_relaxed);
+    if (c <= 0 || l <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        if (hipDeviceGetAttribute(&l, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess ||
+            l <= 0)
+            l = 160 * 1024;
+        g_cus[dev].store(c, std::memory_order_relaxed);
+        g_lds[dev].store(l, std::memory_order_relaxed);
+    }
+    *cus = c;
+    *lds = l;
+}
+
+}  // namespace
+
+namespace vrt {
+
+int launch_gate(hipError_t* e) {
+    ++g_launches;
+    if (g_fail_at > 0 && g_launches == g_fail_at) {
+        *e = hipErrorLaunchFailure;
+        return 0;
+    }
+    if (g_dry) {
+        *e = hipSuccess;
+        return 0;
+    }
+    return 1;
+}
+
+int device_cus() {
+    int c, l;
+    device_props(&c, &l);
+    return c;
+}
+
+int device_lds() {
+    int c, l;
+    device_props(&c, &l);
+    return l;
+}
+
+}  // namespace vrt
 
 namespace {
 
@@ -48,16 +114,18 @@ thread_local hipEvent_t g_ev_start = nullptr;
 thread_local hipEvent_t g_ev_stop = nullptr;
 
 hipError_t record_start(hipStream_t s) {
-    return g_ev_start ? hipEventRecord(g_ev_start, s) : hipSuccess;
+    return g_ev_start && !g_dry ? hipEventRecord(g_ev_start, s) : hipSuccess;
 }
 hipError_t record_stop(hipStream_t s) {
-    return g_ev_stop ? hipEventRecord(g_ev_stop, s) : hipSuccess;
+    return g_ev_stop && !g_dry ? hipEventRecord(g_ev_stop, s) : hipSuccess;
 }
 
 // A HIP error code is sticky per thread: an earlier failed runtime call made
 // by someone else would otherwise be reported after our own launch.  Clear it
 // once before a call enqueues anything.
-void clear_sticky_error() { (void)hipGetLastError(); }
+void clear_sticky_error() {
+    if (!g_dry) (void)hipGetLastError();
+}
 
 int elem_bytes(const vrt_cache_desc& d) { return d.dtype == VRT_BF16 ? 2 : 4; }
 
@@ -152,14 +220,8 @@ float scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)
 // round of workgroups (as many per CU as the kernel's LDS allows, at most 4),
 // so each workgroup streams a long run of tiles through one pipeline.
 int pick_hg(const Geom& g, long long units, int rows_per_head, long long qchunks, long long splits) {
-    int dev = 0, cus = 0, lds = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
-        lds <= 0)
-        lds = 160 * 1024;
+    int cus, lds;
+    device_props(&cus, &lds);
     const int elem = g.dtype == 1 ? 2 : 4;
     const long long wg_lds = (long long)attn_stages(g.dtype, g.D, splits > 1) * 2 * kTile * g.D * elem +
                              kQsBytes + 4 * kTile * elem;
@@ -202,6 +264,26 @@ void attn_shape(const Geom& g, bool mfma, long long units, int n, AttnArgs* at) 
     // itself; otherwise a separate append launch runs first
     at->append = at->n_qchunks == 1 ? 1 : 0;
     at->hg = pick_hg(g, units, std::min(at->qchunk, n) * g.group, at->n_qchunks, 1);
+}
+
+// Attention launch parameters of a decoder sub-batch of m tokens over
+// `units` units: a single token is split over keys (split-K, merged after),
+// a prefill is not.
+void dec_shape(const Geom& g, long long units, int m, AttnArgs* at) {
+    at->split_len = kSplitLen;
+    at->scale_log2 = scale_log2(g.D);
+    if (m == 1) {
+        at->qchunk = 1;
+        at->n_qchunks = 1;
+        at->n_splits = (g.window + kSplitLen - 2) / kSplitLen + 1;
+    } else {
+        at->partials = nullptr;
+        at->qchunk = kRows / g.group;
+        at->n_qchunks = (m + at->qchunk - 1) / at->qchunk;
+        at->n_splits = 1;
+    }
+    at->append = at->n_qchunks == 1 ? 1 : 0;
+    at->hg = pick_hg(g, units, std::min(at->qchunk, m) * g.group, at->n_qchunks, at->n_splits);
 }
 
 hipError_t launch_attn(const AttnArgs& at, bool mfma, const StateTable& t, hipStream_t s) {
@@ -451,6 +533,32 @@ int vrt_attn_path(const vrt_cache_desc* desc, int n) {
     return use_mfma(*desc, n) ? 1 : 0;
 }
 
+vrt_status vrt_attn_plan(const vrt_cache_desc* desc, int64_t units, int n, int32_t* heads_per_group,
+                         int32_t* n_splits, int32_t* n_qchunks) {
+    const vrt_status s = check_desc(desc);
+    if (s != VRT_OK) return s;
+    if (units < 1 || units > ((int64_t)1 << 40) || n < 1 || !heads_per_group || !n_splits || !n_qchunks)
+        return VRT_ERR_INVALID;
+    const Geom g = make_geom(*desc);
+    AttnArgs at{};
+    if (desc->kind == VRT_DEC_MODRING)
+        dec_shape(g, (long long)units, n, &at);
+    else
+        attn_shape(g, use_mfma(*desc, n), (long long)units, n, &at);
+    *heads_per_group = at.hg;
+    *n_splits = at.n_splits;
+    *n_qchunks = at.n_qchunks;
+    return VRT_OK;
+}
+
+void vrt_test_launch_hook(int32_t fail_at, int32_t dry_run) {
+    g_fail_at = fail_at > 0 ? fail_at : 0;
+    g_dry = dry_run ? 1 : 0;
+    g_launches = 0;
+}
+
+int64_t vrt_test_launch_count(void) { return g_launches; }
+
 size_t vrt_offline_scratch_bytes(const vrt_cache_desc* desc, int T) {
     if (check_desc(desc) != VRT_OK || T < 1) return 0;
     return 2 * (size_t)desc->n_heads_kv * (size_t)T * desc->head_dim * elem_bytes(*desc);
@@ -665,7 +773,6 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int laye
         }
 
     const Geom g = make_geom(d);
-    const int n_splits = (d.window + kSplitLen - 2) / kSplitLen + 1;
     clear_sticky_error();
     int t0 = 0;
     for (int m : subs) {
@@ -685,22 +792,8 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int laye
             at.k = k;
             at.v = v;
             at.out = out;
-            at.split_len = kSplitLen;
-            at.scale_log2 = scale_log2(d.head_dim);
-            if (m == 1) {
-                at.partials = (float*)workspace;
-                at.qchunk = 1;
-                at.n_qchunks = 1;
-                at.n_splits = n_splits;
-            } else {
-                at.partials = nullptr;
-                at.qchunk = kRows / g.group;
-                at.n_qchunks = (m + at.qchunk - 1) / at.qchunk;
-                at.n_splits = 1;
-            }
-            at.append = at.n_qchunks == 1 ? 1 : 0;
-            at.hg = pick_hg(g, (long long)um.n_states * um.nl, std::min(at.qchunk, m) * g.group,
-                            at.n_qchunks, at.n_splits);
+            at.partials = m == 1 ? (float*)workspace : nullptr;
+            dec_shape(g, (long long)um.n_states * um.nl, m, &at);
             hipError_t err = hipSuccess;
             if (!at.append) err = note(launch_rope_append(aa, t, stream));
             if (err == hipSuccess) err = note(record_start(stream));
@@ -795,6 +888,9 @@ vrt_status vrt_enc_block_feed(vrt_stream_state* const* st, int n_states, int lay
     if (!x || !out || !w || !workspace || n_new < 1) return VRT_ERR_INVALID;
     if (!w->norm_w || !w->w_qkv || !w->w_o || w->reserved != 0) return VRT_ERR_INVALID;
     if (!(w->eps >= 0.f) || !std::isfinite(w->eps)) return VRT_ERR_INVALID;
+    // (left, right) windows answer other frames' queries than the rows fed,
+    // so the residual rows would not line up: the block takes the rings only
+    if (d.kind == VRT_ENC_LOOKAHEAD) return VRT_ERR_UNSUPPORTED;
     if (d.dtype != VRT_BF16 || d.n_heads_q != d.n_heads_kv) return VRT_ERR_UNSUPPORTED;
     const int dim = d.n_heads_q * d.head_dim;
     if (dim % 128 != 0 || dim > 2048) return VRT_ERR_UNSUPPORTED;
@@ -814,7 +910,10 @@ vrt_status vrt_enc_block_feed(vrt_stream_state* const* st, int n_states, int lay
     char *y = ws, *q = ws + bb, *k = ws + 2 * bb, *v = ws + 3 * bb, *a = ws + 4 * bb;
     clear_sticky_error();
     NormArgs na{x, dim, w->norm_w, y, dim, M, dim, w->eps};
-    if (note(launch_rmsnorm(na, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    if (note(launch_rmsnorm(na, stream)) != hipSuccess) {
+        poison(st, n_states);
+        return VRT_ERR_DEVICE;
+    }
     GemmArgs g{};
     g.A = y;
     g.lda = dim;
@@ -829,7 +928,12 @@ vrt_status vrt_enc_block_feed(vrt_stream_state* const* st, int n_states, int lay
     g.seg[0] = GemmSeg{q, w->b_q, dim};
     g.seg[1] = GemmSeg{k, nullptr, dim};
     g.seg[2] = GemmSeg{v, w->b_v, dim};
-    if (note(launch_gemm(g, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    if (note(launch_gemm(g, stream)) != hipSuccess) {
+        poison(st, n_states);
+        return VRT_ERR_DEVICE;
+    }
+    // every check of the feed was made above, so it can only fail on a
+    // launch, and then it has poisoned the states itself
     s = vrt_enc_attn_feed(st, n_states, layer, 1, q, k, v, n_new, a, stream);
     if (s != VRT_OK) return s;
     GemmArgs o{};
@@ -846,7 +950,11 @@ vrt_status vrt_enc_block_feed(vrt_stream_state* const* st, int n_states, int lay
     o.seg_w = dim;
     o.n_seg = 1;
     o.seg[0] = GemmSeg{out, w->b_o, dim};
-    if (note(launch_gemm(o, stream)) != hipSuccess) return VRT_ERR_DEVICE;
+    if (note(launch_gemm(o, stream)) != hipSuccess) {
+        // the rings already hold this feed's rows: a retry would append them twice
+        poison(st, n_states);
+        return VRT_ERR_DEVICE;
+    }
     return VRT_OK;
 }
 

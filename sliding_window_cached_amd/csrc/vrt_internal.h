@@ -7,6 +7,26 @@
 
 namespace vrt {
 
+// Every kernel launch of the library goes through this gate first.  It
+// returns 1 to go ahead; 0 to skip the launch with *e as its result: the
+// launch the testing hook (vrt_test_launch_hook) marks to fail gets a launch
+// error, and in the hook's dry-run mode every other launch is skipped and
+// reported successful (host logic without a GPU).
+int launch_gate(hipError_t* e);
+// Compute units and LDS bytes per compute unit of the current device, read
+// once per device (256 and 160 KB, MI355X's, when no device answers).
+int device_cus();
+int device_lds();
+#define VRT_LAUNCH(KERNEL, ...)                                      \
+    do {                                                             \
+        hipError_t gate_e_;                                          \
+        if (::vrt::launch_gate(&gate_e_)) {                          \
+            hipLaunchKernelGGL(KERNEL, __VA_ARGS__);                 \
+            gate_e_ = hipGetLastError();                             \
+        }                                                            \
+        if (gate_e_ != hipSuccess) return gate_e_;                   \
+    } while (0)
+
 // States per launch.  The per-state table travels in the kernel arguments
 // (no device-side table to upload, nothing for the library to allocate);
 // 256 entries (one launch for 256 streams) make a 6 KB argument block;

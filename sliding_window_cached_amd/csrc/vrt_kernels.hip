@@ -1291,11 +1291,11 @@ hipError_t launch_rope_append(const AppendArgs& a, const StateTable& t, hipStrea
     const dim3 grid((unsigned)(a.m.n_states * a.m.nl * nfb));
     VRT_DISPATCH_ED(a.g.dtype, a.g.D, {
         if (a.g.mod)
-            hipLaunchKernelGGL((k_rope_append<E_, D_, true>), grid, dim3(256), 0, s, a, t);
+            VRT_LAUNCH((k_rope_append<E_, D_, true>), grid, dim3(256), 0, s, a, t);
         else
-            hipLaunchKernelGGL((k_rope_append<E_, D_, false>), grid, dim3(256), 0, s, a, t);
+            VRT_LAUNCH((k_rope_append<E_, D_, false>), grid, dim3(256), 0, s, a, t);
     });
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t s) {
@@ -1309,16 +1309,16 @@ hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t 
 #define VRT_ATTN(MOD, SPLIT, APP)                                                                   \
     do {                                                                                            \
         if (one)                                                                                    \
-            hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, 1, false>), grid, block, 0, s, a, t); \
+            VRT_LAUNCH((k_attn<E_, D_, MOD, SPLIT, APP, 1, false>), grid, block, 0, s, a, t); \
         else                                                                                        \
-            hipLaunchKernelGGL((k_attn<E_, D_, MOD, SPLIT, APP, kRows / 4, false>), grid, block, 0, s, a, t); \
+            VRT_LAUNCH((k_attn<E_, D_, MOD, SPLIT, APP, kRows / 4, false>), grid, block, 0, s, a, t); \
     } while (0)
 #define VRT_LOOK(MOD, APP)                                                                          \
     do {                                                                                            \
         if (one)                                                                                    \
-            hipLaunchKernelGGL((k_attn<E_, D_, MOD, false, APP, 1, true>), grid, block, 0, s, a, t); \
+            VRT_LAUNCH((k_attn<E_, D_, MOD, false, APP, 1, true>), grid, block, 0, s, a, t); \
         else                                                                                        \
-            hipLaunchKernelGGL((k_attn<E_, D_, MOD, false, APP, kRows / 4, true>), grid, block, 0, s, a, t); \
+            VRT_LAUNCH((k_attn<E_, D_, MOD, false, APP, kRows / 4, true>), grid, block, 0, s, a, t); \
     } while (0)
     // windows without rotation: no splits; the fused append needs one query chunk
     if (!a.g.rope && (split || (app && a.n_qchunks != 1))) return hipErrorInvalidValue;
@@ -1336,15 +1336,15 @@ hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t 
     });
 #undef VRT_ATTN
 #undef VRT_LOOK
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t s) {
     if (a.g.dtype != 1 || a.g.D != 64 || a.g.group != 1 || a.n_splits != 1)
         return hipErrorInvalidValue;
     const long long blocks = (long long)a.m.n_states * a.m.nl * a.g.hkv * a.n_qchunks;
-    hipLaunchKernelGGL(k_attn_mfma, dim3((unsigned)blocks), dim3(256), 0, s, a, t);
-    return hipGetLastError();
+    VRT_LAUNCH(k_attn_mfma, dim3((unsigned)blocks), dim3(256), 0, s, a, t);
+    return hipSuccess;
 }
 
 hipError_t launch_pend_save(const AttnArgs& a, const StateTable& t, int keep, hipStream_t s) {
@@ -1353,25 +1353,25 @@ hipError_t launch_pend_save(const AttnArgs& a, const StateTable& t, int keep, hi
     const long long bpu = (row / 16 + 63) / 64;
     const dim3 grid((unsigned)((long long)a.m.n_states * a.m.nl * bpu));
     VRT_DISPATCH_ED(a.g.dtype, a.g.D, {
-        hipLaunchKernelGGL((k_pend_save<E_, D_>), grid, dim3(64), 0, s, a, t, keep);
+        VRT_LAUNCH((k_pend_save<E_, D_>), grid, dim3(64), 0, s, a, t, keep);
     });
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_dec_combine(const AttnArgs& a, const StateTable& t, hipStream_t s) {
     const dim3 grid((unsigned)(a.m.n_states * a.m.nl * a.g.hq));
     VRT_DISPATCH_ED(a.g.dtype, a.g.D, {
-        hipLaunchKernelGGL((k_dec_combine<E_, D_>), grid, dim3(64), 0, s, a, t);
+        VRT_LAUNCH((k_dec_combine<E_, D_>), grid, dim3(64), 0, s, a, t);
     });
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_compact(const CompactArgs& a, const CompactTable& t, hipStream_t s) {
     const dim3 grid((unsigned)(a.n_entries * a.g.hkv * 2));
     VRT_DISPATCH_ED(a.g.dtype, a.g.D, {
-        hipLaunchKernelGGL((k_compact<E_, D_>), grid, dim3(256), 0, s, a, t);
+        VRT_LAUNCH((k_compact<E_, D_>), grid, dim3(256), 0, s, a, t);
     });
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace vrt

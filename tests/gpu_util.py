@@ -3,7 +3,15 @@ the error measures the parity bar is written in.
 
 Tolerances (written in the tests): fp32 storage, norm-wise relative error
 max|gpu - oracle| / max|oracle| <= 1e-5 per output tensor; bf16 storage,
-max-abs error <= 2e-2 (the relative figure is reported beside it)."""
+max-abs error <= 2e-2 and, since with inputs of scale 0.5 the outputs are
+only a few hundredths in size, also the norm-wise relative error
+max|gpu - oracle| / max|oracle| <= 1e-2.  The relative bound comes from the
+bf16 roundings of the rotated q and k, the softmax weights and the output:
+each is an unbiased round-to-nearest-even with relative error at most 2^-9,
+the roundings of different keys are independent, so over a window their
+effect on an output adds in quadrature and stays a small multiple of 2^-9
+(about 2e-3) of the output scale; a wrong key, position or weight moves an
+output by a sizeable fraction of it."""
 from __future__ import annotations
 
 import sys
@@ -17,6 +25,7 @@ from synth import qkv
 DEV = torch.device("cuda:0")
 F32_TOL = 1e-5
 BF16_TOL = 2e-2
+BF16_REL_TOL = 1e-2
 
 
 def say(*a):
@@ -57,8 +66,10 @@ def check_close(a, ref, dtype, what=""):
         assert e <= F32_TOL, (what, e)
     else:
         e, r = abs_err(a, ref), rel_err(a, ref)
-        say(f"  {what}: bf16 max-abs err {e:.3e} (tol {BF16_TOL:g}), rel {r:.3e}")
+        say(f"  {what}: bf16 max-abs err {e:.3e} (tol {BF16_TOL:g}), rel {r:.3e} "
+            f"(tol {BF16_REL_TOL:g})")
         assert e <= BF16_TOL, (what, e)
+        assert r <= BF16_REL_TOL, (what, r)
 
 
 class Pool:

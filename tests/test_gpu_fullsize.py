@@ -5,7 +5,8 @@ Steady-state serving (vector path): 256 streams x 1 layer, bf16 N(0,1)*0.5,
 start positions U[1e4, 1e6), rings pre-filled with 750 frames, then 4-frame
 feeds of all 256 streams in one call, across a compaction.
 Catch-up (matrix path): 1 stream x 32 layers, bf16 N(0,1), 15300 frames in
-29 feeds of 512 and one of 452, compactions between feeds.
+29 feeds of 512 and one of 452, compactions between feeds; three layers are
+also run offline over the whole 15300 frames and must match bit for bit.
 
 Inputs are drawn on the GPU from seeded generators; the rows checked and the
 windows they read are copied to the host for the oracle.  Bar: max-abs error
@@ -105,6 +106,18 @@ def test_catchup_32_layers_sampled():
     assert len(r.events) == 27
     for l in range(L):
         assert st.query(l) == (r.abs_base, r.n_kv), l
+    # the whole sequence offline (T = 15300, the same matrix-path kernel over a
+    # linear scratch): bit-identical to the 512-frame feeds with their 27
+    # compactions, on three layers (streaming-plan page, Verification item 1)
+    sb = vrt.offline_scratch_bytes(desc, T)
+    scratch = torch.empty(sb, dtype=torch.uint8, device=DEV)
+    off = torch.empty((T, H, D), dtype=torch.bfloat16, device=DEV)
+    for l in (0, 13, 31):
+        say(f"offline T={T}, layer {l}")
+        vrt.enc_attn_offline(desc, q[0, l], k[0, l], v[0, l], T, start, off, scratch, sb, stream())
+        torch.cuda.synchronize()
+        assert torch.equal(off, out[0, l]), f"offline != streamed, layer {l}"
+    del scratch, off
     rng = np.random.default_rng(6)
     for l in (0, 13, 31):
         ts = sorted({0, 511, 512, 1535, 1536, 7000, T - 453, T - 452, T - 1}
