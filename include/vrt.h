@@ -272,6 +272,25 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* states, int n_states, int 
                              int n_tok, void* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* The decode step of vrt_dec_attn_step without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the split-K
+ * partials go to a static device array inside the library, 128 MiB on each
+ * device it runs on, held until the process ends; this call itself
+ * allocates nothing (its first call on a device looks the array's address
+ * up).  The same kernels and arithmetic as vrt_dec_attn_step, so the outputs
+ * are bit-identical.  n_tok = 1 needs vrt_dec_workspace_bytes(desc,
+ * n_states, n_layers, 1) <= 128 MiB (VRT_ERR_CAPACITY otherwise; the
+ * 32-stream x 26-layer step at window 8192 needs 118.8 MiB); n_tok > 1 (a
+ * prefill) uses no partials.  Nothing in the array has to start at zero:
+ * the merge reads only the splits the same call wrote.  Every call on one
+ * device shares that device's array and it keeps the last call's contents,
+ * so calls that overlap on one device (different host threads or streams
+ * without ordering between them) race and must not be made. */
+vrt_status vrt_dec_attn_step_static(vrt_stream_state* const* states, int n_states, int layer0,
+                                    int n_layers, const void* q, const void* k, const void* v,
+                                    int n_tok, void* out, hipStream_t stream);
+
 /* ---- The attention half of an encoder block around the path (family doc,
  * "Architecture (summary)", Encoder bullet: pre-norm RMSNorm blocks, NEOX
  * RoPE, the causal 750-frame sliding window, biases on q, v and o and none on

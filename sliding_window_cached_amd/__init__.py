@@ -34,7 +34,7 @@ EXPORTS = (
     "vrt_conv_stem_device_bytes", "vrt_conv_stem_create", "vrt_conv_stem_reset",
     "vrt_conv_stem_destroy", "vrt_conv_stem_query", "vrt_conv_out_frames",
     "vrt_conv_workspace_bytes", "vrt_conv_stem_feed", "vrt_read_probe", "vrt_attn_plan",
-    "vrt_test_launch_hook", "vrt_test_launch_count",
+    "vrt_test_launch_hook", "vrt_test_launch_count", "vrt_dec_attn_step_static",
 )
 
 
@@ -154,6 +154,7 @@ def _load():
         "vrt_dec_attn_step": (c_int, [POINTER(P), c_int, c_int, c_int, P, P, P, c_int, P, P,
                                       c_size_t, P]),
         "vrt_set_attn_events": (c_int, [P, P]),
+        "vrt_dec_attn_step_static": (c_int, [POINTER(P), c_int, c_int, c_int, P, P, P, c_int, P, P]),
         "vrt_rmsnorm": (c_int, [P, c_int, c_int, P, ctypes.c_float, P, P]),
         "vrt_linear": (c_int, [P, c_int, c_int, P, c_int, P, P, P, P]),
         "vrt_block_workspace_bytes": (c_size_t, [POINTER(CacheDesc), c_int]),
@@ -332,6 +333,16 @@ def dec_attn_step(states, layer0, n_layers, q, k, v, n_tok, out, workspace=None,
                               _ptr(v), n_tok, _ptr(out), _ptr(workspace), ws_bytes, stream)
     if check:
         _check(s, "dec_attn_step")
+    return s
+
+
+def dec_attn_step_static(states, layer0, n_layers, q, k, v, n_tok, out, stream=0, check=True):
+    """The decode step with its partials in the library's static device array
+    (allocates nothing; calls that overlap on one device race)."""
+    s = lib.vrt_dec_attn_step_static(_handles(states), len(states), layer0, n_layers, _ptr(q), _ptr(k),
+                                     _ptr(v), n_tok, _ptr(out), stream)
+    if check:
+        _check(s, "dec_attn_step_static")
     return s
 
 

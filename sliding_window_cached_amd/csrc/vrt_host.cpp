@@ -812,6 +812,26 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int laye
     return VRT_OK;
 }
 
+vrt_status vrt_dec_attn_step_static(vrt_stream_state* const* st, int n_states, int layer0,
+                                    int n_layers, const void* q, const void* k, const void* v,
+                                    int n_tok, void* out, hipStream_t stream) {
+    const vrt_status s = check_batch(st, n_states, layer0, n_layers, VRT_DEC_MODRING);
+    if (s != VRT_OK) return s;
+    if (!q || !k || !v || !out || n_tok < 1) return VRT_ERR_INVALID;
+    if (n_tok > 1)   // a prefill has no partials
+        return vrt_dec_attn_step(st, n_states, layer0, n_layers, q, k, v, n_tok, out, nullptr, 0, stream);
+    const size_t need = vrt_dec_workspace_bytes(&st[0]->d, n_states, n_layers, 1);
+    if (need > kStaticScratchBytes) return VRT_ERR_CAPACITY;
+    void* ws = nullptr;
+    if (g_dry) {
+        ws = (void*)(uintptr_t)256;   // dry run: nothing is launched, nothing is read
+    } else {
+        clear_sticky_error();
+        if (note(static_scratch(&ws)) != hipSuccess) return VRT_ERR_DEVICE;
+    }
+    return vrt_dec_attn_step(st, n_states, layer0, n_layers, q, k, v, 1, out, ws, need, stream);
+}
+
 vrt_status vrt_set_attn_events(hipEvent_t start, hipEvent_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return VRT_ERR_INVALID;
     if (start) {

@@ -245,6 +245,12 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, hipS
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
 
 
+// Bytes of the library's static device scratch array (one per device, held
+// until the process ends), and its device address on the current device:
+// looked up once per device with hipGetSymbolAddress, then reused.
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_rope_append(const AppendArgs& a, const StateTable& t, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t s);

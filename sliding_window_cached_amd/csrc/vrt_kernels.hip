@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "vrt_internal.h"
 
@@ -1275,6 +1276,33 @@ __global__ __launch_bounds__(64) void k_dec_combine(AttnArgs a, StateTable t) {
 }
 
 }  // namespace
+
+// ------------------------------------------------ static scratch array ----
+// Split-K partials of the allocation-free decode step.  In host code the
+// array's name stands for a host-side shadow, not a device address: kernels
+// only ever get the address that hipGetSymbolAddress returns for the current
+// device (each device holds its own copy at its own address).
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static void* addr[kDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // ------------------------------------------------------------ launchers ----
 #define VRT_DISPATCH_ED(dtype, D, BODY)                                        \

@@ -200,3 +200,20 @@ def test_conv_stem_is_unchanged_when_a_launch_fails():
             vrt.test_launch_hook(0, dry_run=True)
             assert vrt.conv_stem_feed(fresh, Q, n_frames, w, O, WS, wsb) >= 0
             assert fresh[1].query() == after
+
+
+def test_static_decode_step_host_logic():
+    """The allocation-free decode step: the same launches as the workspace
+    step, and refused (nothing enqueued) past its 128 MiB of partials."""
+    d = vrt.dec_desc(n_layers=26)
+    sts = states_of(d, 2)
+    vrt.dec_attn_step(sts, 0, 26, Q, K, V, 39, O)
+    vrt.test_launch_hook(0, dry_run=True)
+    assert vrt.dec_attn_step_static(sts, 0, 26, Q, K, V, 1, O, check=False) == vrt.OK
+    assert vrt.test_launch_count() == 2 and sts[1].query(25) == (0, 40)
+    per_state = vrt.dec_workspace_bytes(d, 1, 26, 1)
+    big = states_of(d, (128 << 20) // per_state + 1)
+    vrt.test_launch_hook(0, dry_run=True)
+    assert vrt.dec_attn_step_static(big, 0, 26, Q, K, V, 1, O, check=False) == vrt.ERR_CAPACITY
+    assert vrt.test_launch_count() == 0 and big[0].query(0) == (0, 0)
+    assert vrt.dec_attn_step_static(big[:32], 0, 26, Q, K, V, 1, O, check=False) == vrt.OK
