@@ -242,6 +242,32 @@ def ring_words(desc) -> str:
     return f"{desc.ring_slots}-slot modulo ring (slot = position % {desc.ring_slots}, no compaction)"
 
 
+DEVICE_WARMUP_S = 0.3
+
+
+def device_warmup(seconds: float = None):
+    """Keep the GPU streaming HBM for `seconds` of wall time (the library's
+    read probe over a 1 GiB buffer, untimed) before the warmup steps: on a
+    freshly leased MI355X the first few hundred attention launches run about
+    6 % slower than the steady state (measured: 185 us with 5 warmup steps
+    against 173 us after 200), so a run with few warmup steps would time the
+    clock ramp instead of the kernel.  No state of the workload is touched."""
+    import torch
+    import sliding_window_cached_amd as vrt
+    seconds = DEVICE_WARMUP_S if seconds is None else seconds
+    if seconds <= 0:
+        return
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            vrt.read_probe(buf, buf.numel(), sink, stream)
+        torch.cuda.synchronize()
+    del buf, sink
+
+
 def _timing_events(n):
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -280,6 +306,7 @@ def bench_c2(args):
     Q, K, V = (_randn(gen, (total, S, 1, n, H, D), 0.5, dev) for _ in range(3))
     out = torch.empty((S, 1, n, H, D), dtype=torch.bfloat16, device=dev)
 
+    device_warmup()
     for i in range(args.warmup):
         vrt.enc_attn_feed(states, 0, 1, Q[i], K[i], V[i], n, out, stream)
     torch.cuda.synchronize()
@@ -368,7 +395,7 @@ def bench_c2(args):
                         "N(0,1)*0.5, start positions U[1e4, 1e6)",
             "streams": S, "layers": 1, "frames_per_step": n, "heads": H, "head_dim": D,
             "window": W, "ring_slots": desc.ring_slots, "ring": args.ring,
-            "parallelism": "none (1 GPU)",
+            "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
         },
         "roofline": {
             "bound": "hbm",
@@ -429,6 +456,7 @@ def bench_c2b(args):
     out = torch.empty((S, n, dim), dtype=torch.bfloat16, device=dev)
     wsb = vrt.block_workspace_bytes(desc, S * n)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    device_warmup()
     for i in range(args.warmup):
         vrt.enc_block_feed(states, 0, X[i], n, bw, out, ws, wsb, stream)
     torch.cuda.synchronize()
@@ -488,7 +516,7 @@ def bench_c2b(args):
                         "pre-filled to 750 frames, 4 frames per stream per step, x ~ N(0,1), "
                         "random weights, bf16",
             "streams": S, "layers": 1, "frames_per_step": n, "d_model": dim, "window": W,
-            "ring_slots": desc.ring_slots, "ring": args.ring, "parallelism": "none (1 GPU)",
+            "ring_slots": desc.ring_slots, "ring": args.ring, "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
         },
         "roofline": {
             "bound": "hbm",
@@ -536,6 +564,7 @@ def bench_cs(args):
     out = torch.empty((S, n // 2, d), dtype=torch.bfloat16, device=dev)
     wsb = vrt.conv_workspace_bytes(n_mel, d, S, n)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    device_warmup()
     for i in range(args.warmup):
         vrt.conv_stem_feed(stems, mel[i], n, cw, out, ws, wsb, stream)
     torch.cuda.synchronize()
@@ -577,7 +606,7 @@ def bench_cs(args):
                         "128 -> 1280 k3 s1 and 1280 -> 1280 k3 s2 with bias and GELU, padding caches; "
                         "4 encoder frames per stream per step",
             "streams": S, "mel_frames_per_step": n, "n_mel": n_mel, "d_model": d,
-            "parallelism": "none (1 GPU)",
+            "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
         },
         "roofline": {
             "bound": "mfma",
@@ -623,6 +652,7 @@ def bench_cm(args):
         for desc, L, _, states, (Q, K, V), out in pools:
             vrt.enc_attn_feed(states, 0, L, Q[i], K[i], V[i], n, out, stream)
 
+    device_warmup()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -669,7 +699,7 @@ def bench_cm(args):
                         "(left, right) windows (16,4),(16,4),(16,0),(16,0),(16,4),(16,4), no RoPE, "
                         "8 heads x 64, bf16 N(0,1)*0.5; answered frames lag by 3 in the (16,4) layers",
             "streams": S, "layers": 6, "frames_per_step": n, "heads": Hm, "head_dim": Dm,
-            "parallelism": "none (1 GPU)",
+            "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
         },
         "roofline": {
             "bound": "hbm",
@@ -872,6 +902,7 @@ def bench_c1(args):
     log(f"c1: drawing inputs for {total} steps into HBM")
     Q, K, V = (_randn(gen, (total, S, L, n, H, D), 0.5, dev) for _ in range(3))
     out = torch.empty((S, L, n, H, D), dtype=torch.bfloat16, device=dev)
+    device_warmup()
     for i in range(args.warmup):
         vrt.enc_attn_feed(states, 0, L, Q[i], K[i], V[i], n, out, stream)
     torch.cuda.synchronize()
@@ -935,7 +966,7 @@ def bench_c1(args):
                         "staggered ring phases (catch-up of U{0..749} frames, then 750), 4 frames per "
                         "stream per step, all layers in one call",
             "streams": S, "layers": L, "frames_per_step": n, "ring_slots": desc.ring_slots,
-            "ring": args.ring, "parallelism": "none (1 GPU)",
+            "ring": args.ring, "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
             "compactions_timed": sum(nc for step in plan for _, nc in step),
         },
         "roofline": {
@@ -1010,6 +1041,7 @@ def bench_c3(args):
         vrt.enc_attn_feed([st], 0, L, q, k, v, sched[b], outs[sched[b]], stream)
 
     # warmup: whole sequences from a reset ring
+    device_warmup()
     b = 0
     for _ in range(args.warmup):
         feed(b)
@@ -1074,7 +1106,7 @@ def bench_c3(args):
                         "one batch through all 32 layers",
             "streams": 1, "layers": L, "frames": sum(sched), "max_batch": 512, "heads": H,
             "head_dim": D, "window": W, "ring_slots": desc.ring_slots, "ring": args.ring,
-            "parallelism": "none (1 GPU)",
+            "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
         },
         "roofline": {
             "bound": "mfma",
@@ -1162,6 +1194,7 @@ def bench_c4(args):
     K = _randn(gen, (total, S, L, 1, HK, DD), 1.0, dev)
     V = _randn(gen, (total, S, L, 1, HK, DD), 1.0, dev)
     out = torch.empty((S, L, 1, HQ, DD), dtype=torch.bfloat16, device=dev)
+    device_warmup()
     for j in range(args.warmup):
         vrt.dec_attn_step(states, 0, L, Q[j], K[j], V[j], 1, out, ws, wsb, stream)
     torch.cuda.synchronize()
@@ -1206,7 +1239,7 @@ def bench_c4(args):
                         "modulo ring 8192, bf16 N(0,1); contexts 24 x U[39, 8192] and 8 x "
                         "U[8193, 10269]; one step = one token per stream",
             "streams": S, "layers": L, "heads_q": HQ, "heads_kv": HK, "head_dim": DD, "window": WIN,
-            "contexts": ctx, "parallelism": "none (1 GPU)",
+            "contexts": ctx, "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
         },
         "roofline": {
             "bound": "hbm",
@@ -1231,6 +1264,9 @@ def main():
     ap.add_argument("--config", default="c2",
                     choices=["c1", "c2", "c2b", "c3", "c4", "cs", "cm", "copy", "read"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--device-warmup", type=float, default=DEVICE_WARMUP_S,
+                    help="seconds of untimed HBM streaming before the warmup steps (0: none; "
+                         "profiler runs use 0 to keep the trace small)")
     ap.add_argument("--ring", default="compact", choices=["compact", "mod"],
                     help="encoder configs: compacting ring (the pages') or modulo ring")
     ap.add_argument("--timing-every", type=int, default=None,
@@ -1242,6 +1278,7 @@ def main():
               "shard across GPUs with no exchange; a single GPU is run and reported.",
               file=sys.stderr)
         sys.exit(2)
+    globals()["DEVICE_WARMUP_S"] = max(0.0, args.device_warmup)
     if not args.no_cpu_baseline and args.config in ("c1", "c2", "c3"):
         start_cpu_pool()    # before anything touches the GPU
     if args.config == "copy":
