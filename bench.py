@@ -627,13 +627,13 @@ def bench_cm(args):
     """The moonshine streaming encoder's attention pattern on the same
     kernels: 256 streams, 4 new frames per stream per step through six layers
     with (left, right) windows (16,4),(16,4),(16,0),(16,0),(16,4),(16,4), no
-    rotation; 8 heads of 64 (the pages' tiny model has heads of 40, which
-    these kernels do not take), bf16 N(0,1)*0.5."""
+    rotation; 8 heads of 40 (the streaming-tiny model's, hidden 320; the ring
+    rows are padded to 64 elements), bf16 N(0,1)*0.5."""
     import torch
     import sliding_window_cached_amd as vrt
 
     dev = torch.device("cuda:0")
-    S, n, Hm, Dm = 256, 4, 8, 64
+    S, n, Hm, Dm = 256, 4, 8, 40
     groups = [(vrt.lookahead_desc(16, 4, n_layers=4, heads=Hm, head_dim=Dm), 4),
               (vrt.lookahead_desc(16, 0, n_layers=2, heads=Hm, head_dim=Dm), 2)]
     stream = torch.cuda.current_stream().cuda_stream
@@ -643,8 +643,9 @@ def bench_cm(args):
     pools = []
     for desc, L in groups:
         nb = vrt.state_device_bytes(desc)
-        mem = torch.empty(S * nb, dtype=torch.uint8, device=dev)
-        states = [vrt.StreamState(desc, mem[i * nb:(i + 1) * nb], nb, 0) for i in range(S)]
+        stride = (nb + 255) // 256 * 256    # each state's memory 256-byte aligned
+        mem = torch.empty(S * stride, dtype=torch.uint8, device=dev)
+        states = [vrt.StreamState(desc, mem[i * stride:i * stride + nb], nb, 0) for i in range(S)]
         qkv = [_randn(gen, (total, S, L, n, Hm, Dm), 0.5, dev) for _ in range(3)]
         pools.append((desc, L, mem, states, qkv, torch.empty((S, L, n, Hm, Dm), dtype=torch.bfloat16, device=dev)))
 
@@ -676,7 +677,8 @@ def bench_cm(args):
             st.close()
     row = Hm * Dm * 2
     # per (stream, layer): q, k, v read, K/V appended, the keys of the union
-    # window read (15 + F + n rows of K and V), outputs written
+    # window read (15 + F + n rows of K and V), outputs written, all at the
+    # heads' 40 elements (the ring rows' padding to 64 is not counted)
     nbytes = sum(S * L * (n + 2 * n + 2 * n + 2 * (15 + max(d.lookahead - 1, 0) + n) + n) * row
                  for d, L, *_ in pools)
     t_step = sum(ms) * 1e-3 / len(ms)
@@ -697,7 +699,7 @@ def bench_cm(args):
         "config": {
             "workload": "moonshine-pattern attention: 256 streams, 4 frames per step, 6 layers with "
                         "(left, right) windows (16,4),(16,4),(16,0),(16,0),(16,4),(16,4), no RoPE, "
-                        "8 heads x 64, bf16 N(0,1)*0.5; answered frames lag by 3 in the (16,4) layers",
+                        "8 heads x 40, bf16 N(0,1)*0.5; answered frames lag by 3 in the (16,4) layers",
             "streams": S, "layers": 6, "frames_per_step": n, "heads": Hm, "head_dim": Dm,
             "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
         },
@@ -728,7 +730,7 @@ def cpu_baseline_cm(steps: int, passes: int = 1):
     from synth import qkv
 
     T = 16 + 4 * steps + 3
-    q, k, v = qkv(7, 0, 0, T, 8, 8, 64, 0.5, "bf16")
+    q, k, v = qkv(7, 0, 0, T, 8, 8, 40, 0.5, "bf16")
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -763,22 +765,23 @@ def cpu_baseline_conv(steps: int):
                       f"in fp64 numpy on one thread, {el:.1f} s"}
 
 
-KERNEL_SRCS = [os.path.join(ROOT, "sliding_window_cached_amd", "csrc", f)
-               for f in ("vrt_kernels.hip", "vrt_block.hip")]
+KERNEL_DIR = os.path.join(ROOT, "sliding_window_cached_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 MFMA_BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy.txt")
+# the source file that holds each kernel a record is kept for
+BLOCK_KERNELS = ("k_gemm_qkv", "k_gemm_o", "k_rmsnorm", "k_gemm_conv", "k_gemm_reduce", "k_row_copy")
 
 
-def kernels_sha256() -> str:
-    """First 16 hex digits of the sha256 of the kernel sources, in order
-    (vrt_kernels.hip, then vrt_block.hip): a recorded counter value holds
-    only while both are unchanged."""
+def kernel_source(kernel: str) -> str:
+    return os.path.join(KERNEL_DIR, "vrt_block.hip" if kernel in BLOCK_KERNELS else "vrt_kernels.hip")
+
+
+def source_sha256(path: str) -> str:
+    """First 16 hex digits of the sha256 of one kernel source file: a
+    recorded counter value holds only while that file is unchanged."""
     import hashlib
-    h = hashlib.sha256()
-    for p in KERNEL_SRCS:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def workload_key(args, name: str) -> str:
@@ -798,13 +801,13 @@ def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from the rocprofv3
     FETCH_SIZE / WRITE_SIZE runs recorded in profiles/hbm_traffic.txt
     (already scaled by the copy-kernel calibration there), or None when no
-    record exists or the kernel source changed since it was taken."""
+    record exists or the kernel's source changed since it was taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    sha = kernels_sha256()
+    sha = source_sha256(kernel_source(kernel))
     for line in open(TRAFFIC_FILE):
         f = line.split()
-        if len(f) == 5 and f[0] == kernel and f[1] == workload and f[4] == f"kernels_sha256={sha}":
+        if len(f) == 5 and f[0] == kernel and f[1] == workload and f[4] == f"src_sha256={sha}":
             return {"fetch_bytes": float(f[2]), "write_bytes": float(f[3]),
                     "bytes": float(f[2]) + float(f[3])}
     return None
@@ -813,14 +816,14 @@ def measured_traffic(kernel: str, workload: str):
 def measured_mfma_busy(kernel: str, workload: str):
     """Fraction of the launch the matrix cores were busy, from the rocprofv3
     SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE run recorded in
-    profiles/mfma_busy.txt, or None when no record exists or the kernel
+    profiles/mfma_busy.txt, or None when no record exists or the kernel's
     source changed since it was taken."""
     if not os.path.exists(MFMA_BUSY_FILE):
         return None
-    sha = kernels_sha256()
+    sha = source_sha256(kernel_source(kernel))
     for line in open(MFMA_BUSY_FILE):
         f = line.split()
-        if len(f) == 4 and f[0] == kernel and f[1] == workload and f[3] == f"kernels_sha256={sha}":
+        if len(f) == 4 and f[0] == kernel and f[1] == workload and f[3] == f"src_sha256={sha}":
             return float(f[2])
     return None
 

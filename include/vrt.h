@@ -95,14 +95,19 @@ typedef enum {
  * frames.  A query is answered once its last future frame has been fed; the
  * queries still waiting keep their q rows in the state.  rope_theta must be
  * 0; ring_slots >= window + F + max_batch - 1 (F = future frames), a
- * multiple of 64.  Layers with different windows use different descs. */
+ * multiple of 64.  Layers with different windows use different descs.
+ * Its head_dim may also be a multiple of 8 below 64 (the streaming-tiny
+ * model's 8 heads of 40, moonshine forward map, "Variant Notes"): inputs,
+ * outputs and waiting q rows keep head_dim elements per head, the ring rows
+ * are stored padded with zeros to 64 elements, and the softmax scale is
+ * 1/sqrt(head_dim). */
 typedef struct {
     int32_t kind;        /* vrt_cache_kind */
     int32_t dtype;       /* vrt_dtype: storage and I/O type; accumulation is fp32 */
     int32_t n_layers;    /* layers held by one state (>= 1) */
     int32_t n_heads_q;   /* query heads (multiple of n_heads_kv) */
     int32_t n_heads_kv;  /* key/value heads */
-    int32_t head_dim;    /* 64 or 128 */
+    int32_t head_dim;    /* 64 or 128; ENC_LOOKAHEAD also a multiple of 8 below 64 */
     int32_t window;      /* W: a query at p sees keys in (p - W, p] */
     int32_t ring_slots;  /* ENC_RING: >= window + max_batch; DEC_MODRING: >= window,
                             multiple of 64; ENC_MODRING: >= window - 1 + max_batch,
@@ -127,7 +132,8 @@ const char* vrt_last_device_error(void);
 /* Check a descriptor without creating anything.  VRT_ERR_INVALID for
  * non-positive sizes, a nonzero lookahead outside ENC_LOOKAHEAD, or a
  * nonzero rope_theta inside it; VRT_ERR_UNSUPPORTED for a
- * head_dim other than 64/128, an unknown dtype/kind, an ENC_RING ring smaller
+ * head_dim other than 64/128 (or, for ENC_LOOKAHEAD, a multiple of 8 below
+ * 64), an unknown dtype/kind, an ENC_RING ring smaller
  * than window + max_batch (streaming-plan page, "Unbounded length": batches
  * of at most 512 frames so one feed can never overflow the 1536-slot ring),
  * a decoder ring smaller than the window or not a multiple of 64, an
@@ -137,14 +143,16 @@ const char* vrt_last_device_error(void);
 vrt_status vrt_desc_check(const vrt_cache_desc* desc);
 
 /* Device bytes one state needs: for each layer a K ring and a V ring, each
- * [n_heads_kv][ring_slots][head_dim] elements; for ENC_LOOKAHEAD then, per
- * layer, F rows of n_heads_q * head_dim elements of waiting queries.  0 if
- * the desc is invalid. */
+ * [n_heads_kv][ring_slots][row] elements, row = head_dim (64 for a
+ * lookahead head_dim below 64); for ENC_LOOKAHEAD then, per layer, F rows of
+ * n_heads_q * head_dim elements of waiting queries.  0 if the desc is
+ * invalid. */
 size_t vrt_state_device_bytes(const vrt_cache_desc* desc);
 
 /* Byte offset, inside a state's device memory, of row 0 of the ring slice
- * (layer, which = 0 for K / 1 for V, kv head).  Rows are head_dim elements;
- * slot s of that slice starts at offset + s * head_dim * elem_size.  K rows
+ * (layer, which = 0 for K / 1 for V, kv head).  Rows are head_dim elements
+ * (64, zero-padded, for a lookahead head_dim below 64); slot s of that slice
+ * starts at offset + s * row * elem_size.  K rows
  * hold RoPE-rotated keys, V rows the values as given.  (size_t)-1 on bad
  * arguments. */
 size_t vrt_ring_offset(const vrt_cache_desc* desc, int layer, int which, int kv_head);

@@ -151,7 +151,11 @@ vrt_status check_desc(const vrt_cache_desc* d) {
     if (d->n_heads_q % d->n_heads_kv != 0) return VRT_ERR_INVALID;
     if (look ? d->rope_theta != 0.0 : (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta)))
         return VRT_ERR_INVALID;
-    if (d->head_dim != 64 && d->head_dim != 128) return VRT_ERR_UNSUPPORTED;
+    // head_dim 64 or 128; the lookahead kind (no rotation) also takes any
+    // multiple of 8 below 64, its ring rows padded to 64 elements
+    if (d->head_dim != 64 && d->head_dim != 128 &&
+        !(look && d->head_dim >= 8 && d->head_dim < 64 && d->head_dim % 8 == 0))
+        return VRT_ERR_UNSUPPORTED;
     const int group = d->n_heads_q / d->n_heads_kv;
     if (group > kRows) return VRT_ERR_UNSUPPORTED;
     if (d->ring_slots > (1 << 24) || d->window > (1 << 24) || d->max_batch > (1 << 20))
@@ -188,15 +192,20 @@ size_t pend_layer_bytes(const vrt_cache_desc& d) {
     return (size_t)look_f(d) * d.n_heads_q * d.head_dim * (d.dtype == VRT_BF16 ? 2 : 4);
 }
 
+// elements per ring row: head_dim, or 64 for a lookahead head_dim below 64
+// (rows padded with zeros, so the kernels see a 64-element head)
+int ring_dim(const vrt_cache_desc& d) { return d.head_dim < 64 ? 64 : d.head_dim; }
+
 size_t slice_bytes(const vrt_cache_desc& d) {
-    return (size_t)d.ring_slots * d.head_dim * elem_bytes(d);
+    return (size_t)d.ring_slots * ring_dim(d) * elem_bytes(d);
 }
 size_t layer_bytes(const vrt_cache_desc& d) { return 2 * (size_t)d.n_heads_kv * slice_bytes(d); }
 
 Geom make_geom(const vrt_cache_desc& d) {
     Geom g;
     g.dtype = d.dtype;
-    g.D = d.head_dim;
+    g.D = ring_dim(d);
+    g.Dio = d.head_dim;
     g.hq = d.n_heads_q;
     g.hkv = d.n_heads_kv;
     g.group = d.n_heads_q / d.n_heads_kv;
@@ -212,6 +221,8 @@ Geom make_geom(const vrt_cache_desc& d) {
     return g;
 }
 
+// log2(e) / sqrt(head_dim): the softmax scale of the head as given (40 for a
+// 40-wide head stored in 64-element rows)
 float scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
 
 
@@ -250,7 +261,7 @@ void attn_shape(const Geom& g, bool mfma, long long units, int n, AttnArgs* at) 
     at->partials = nullptr;
     at->n_splits = 1;
     at->split_len = kSplitLen;
-    at->scale_log2 = scale_log2(g.D);
+    at->scale_log2 = scale_log2(g.Dio);
     if (mfma) {
         at->qchunk = kQTileMfma;
         at->n_qchunks = (n + kQTileMfma - 1) / kQTileMfma;
@@ -271,7 +282,7 @@ void attn_shape(const Geom& g, bool mfma, long long units, int n, AttnArgs* at) 
 // a prefill is not.
 void dec_shape(const Geom& g, long long units, int m, AttnArgs* at) {
     at->split_len = kSplitLen;
-    at->scale_log2 = scale_log2(g.D);
+    at->scale_log2 = scale_log2(g.Dio);
     if (m == 1) {
         at->qchunk = 1;
         at->n_qchunks = 1;
@@ -561,7 +572,7 @@ int64_t vrt_test_launch_count(void) { return g_launches; }
 
 size_t vrt_offline_scratch_bytes(const vrt_cache_desc* desc, int T) {
     if (check_desc(desc) != VRT_OK || T < 1) return 0;
-    return 2 * (size_t)desc->n_heads_kv * (size_t)T * desc->head_dim * elem_bytes(*desc);
+    return 2 * (size_t)desc->n_heads_kv * (size_t)T * ring_dim(*desc) * elem_bytes(*desc);
 }
 
 vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const void* k,
@@ -578,7 +589,7 @@ vrt_status vrt_enc_attn_offline(const vrt_cache_desc* desc, const void* q, const
     Geom g = make_geom(*desc);
     g.slots = T;
     g.mod = 0;
-    g.slice_bytes = (long long)T * desc->head_dim * elem_bytes(*desc);
+    g.slice_bytes = (long long)T * ring_dim(*desc) * elem_bytes(*desc);
     g.v_off = (long long)desc->n_heads_kv * g.slice_bytes;
     g.layer_bytes = 2 * g.v_off;
     StateTable t;
@@ -680,7 +691,7 @@ vrt_status vrt_enc_attn_feed(vrt_stream_state* const* st, int n_states, int laye
                 at.partials = nullptr;
                 at.n_splits = 1;
                 at.split_len = kSplitLen;
-                at.scale_log2 = scale_log2(g.D);
+                at.scale_log2 = scale_log2(g.Dio);
                 at.qchunk = kRows / g.group;
                 at.n_qchunks = (n_out_sb + at.qchunk - 1) / at.qchunk;
                 // with one query chunk the attention launch appends the new

@@ -64,7 +64,9 @@ constexpr int attn_stages(int dtype, int D, bool split) {
 // Geometry of one cache kind, shared by every state of a launch.
 struct Geom {
     int dtype;          // 0 f32, 1 bf16
-    int D;              // head_dim
+    int D;              // elements per ring row and per head in the kernels (64 or 128)
+    int Dio;            // head_dim of the inputs and outputs (= D, or below 64 for lookahead
+                        // windows: ring rows zero-padded from Dio to D elements)
     int hq, hkv, group; // query heads, kv heads, hq / hkv
     int slots;          // ring slots per (layer, kv head)
     int window;         // W

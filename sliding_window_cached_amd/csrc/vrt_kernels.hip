@@ -218,7 +218,10 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
     __syncthreads();
     const int hkv = a.g.hkv;
     const long long cu = (long long)t.call_idx[si] * m.nl_call + m.l_off + li;
-    const long long row_elems = (long long)hkv * D;
+    // input rows hold Dio elements per head; ring rows D (a head narrower than
+    // 64, only without rotation, is stored zero-padded)
+    const int Dio = a.g.Dio;
+    const long long row_elems = (long long)hkv * Dio;
     const long long in0 = (cu * m.n_total + m.t0 + f0) * row_elems * E::E;
     const char* kin = (const char*)a.k + in0;
     const char* vin = (const char*)a.v + in0;
@@ -227,10 +230,10 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
         const int c = x % CG, fh = x / CG, h = fh % hkv, f = fh / hkv;
         const long long pos = p0 + f0 + f;
         const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + f0 + f);
-        const char* src = kin + ((long long)f * row_elems + (long long)h * D) * E::E;
-        float x0[4], x1[4], y0[4], y1[4];
-        ld4<E>(src + 4 * c * E::E, x0);
-        ld4<E>(src + (H2 + 4 * c) * E::E, x1);
+        const char* src = kin + ((long long)f * row_elems + (long long)h * Dio) * E::E;
+        float x0[4] = {0.f, 0.f, 0.f, 0.f}, x1[4] = {0.f, 0.f, 0.f, 0.f}, y0[4], y1[4];
+        if (4 * c < Dio) ld4<E>(src + 4 * c * E::E, x0);
+        if (H2 + 4 * c < Dio) ld4<E>(src + (H2 + 4 * c) * E::E, x1);
         if (a.g.rope) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) rope_pair(x0[q], x1[q], cs[f * H2 + 4 * c + q], &y0[q], &y1[q]);
@@ -249,8 +252,9 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a, StateTable t)
         const int c = x % VCH, fh = x / VCH, h = fh % hkv, f = fh / hkv;
         const long long pos = p0 + f0 + f;
         const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + f0 + f);
-        const uint4 val =
-            gld<uint4>(vin + ((long long)f * row_elems + (long long)h * D) * E::E + 16 * c);
+        const uint4 val = 16 * c < Dio * E::E
+                              ? gld<uint4>(vin + ((long long)f * row_elems + (long long)h * Dio) * E::E + 16 * c)
+                              : make_uint4(0u, 0u, 0u, 0u);
         gst<uint4>(layer + a.g.v_off + (long long)h * a.g.slice_bytes + slot * (D * E::E) + 16 * c,
                    val);
     }
@@ -524,8 +528,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     // K/V rows.  One (head, row, 4-pair group) item per thread, so every input
     // load is independent; each thread's first item is loaded before the tile
     // DMAs go out, so those loads do not queue behind the tiles.
-    const long long qrow = (long long)a.g.hq * D;
-    const long long krow = (long long)a.g.hkv * D;
+    // io rows: Dio elements per head (= D except for lookahead heads narrower
+    // than the 64-element ring rows, whose extra dims are zeros)
+    constexpr bool kNarrow = LOOK;
+    const int Dio = kNarrow ? a.g.Dio : D;
+    const long long qrow = (long long)a.g.hq * Dio;
+    const long long krow = (long long)a.g.hkv * Dio;
     const int nkv = t.n_kv[si];
     const int items = hg * R * CG;
     struct Item {
@@ -541,11 +549,21 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         const char* src;
         if (LOOK && qi < npend)   // a waiting q row of this (state, layer)
             src = (const char*)t.ring[si] + a.pend_off + (long long)(m.layer0 + m.l_off + li) * a.pend_layer +
-                  ((long long)qi * qrow + (long long)(g * group + gh) * D) * E::E;
+                  ((long long)qi * qrow + (long long)(g * group + gh) * Dio) * E::E;
         else
-            src = (const char*)a.q + ((cu * m.n_total + frame) * qrow + (long long)(g * group + gh) * D) * E::E;
-        ld4<E>(src + 4 * c * E::E, it.x0);
-        ld4<E>(src + (H2 + 4 * c) * E::E, it.x1);
+            src = (const char*)a.q + ((cu * m.n_total + frame) * qrow + (long long)(g * group + gh) * Dio) * E::E;
+        if (!kNarrow || 4 * c < Dio) {
+            ld4<E>(src + 4 * c * E::E, it.x0);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) it.x0[q] = 0.f;
+        }
+        if (!kNarrow || H2 + 4 * c < Dio) {
+            ld4<E>(src + (H2 + 4 * c) * E::E, it.x1);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) it.x1[q] = 0.f;
+        }
         if (APPEND && !LOOK && appender && gh == 0) {
             const long long kv0 = ((cu * m.n_total + frame) * krow + (long long)g * D) * E::E;
             ld4<E>((const char*)a.k + kv0 + 4 * c * E::E, it.k0);
@@ -626,10 +644,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
                 const int c = x % L::CPR, f = (x / L::CPR) % m.n, hh = x / (L::CPR * m.n);
                 const int g = g0 + hh;
                 const long long slot = MOD ? ((t.p0[si] + f) % a.g.slots) : (long long)(nkv + f);
-                const long long src = ((cu * m.n_total + m.t0 + f) * krow + (long long)g * D) * E::E + 16 * c;
+                const long long src = ((cu * m.n_total + m.t0 + f) * krow + (long long)g * Dio) * E::E + 16 * c;
                 char* kd = layer + (long long)g * a.g.slice_bytes + slot * L::RB + 16 * c;
-                const uint4 kk = gld<uint4>((const char*)a.k + src);
-                const uint4 vv = gld<uint4>((const char*)a.v + src);
+                const bool in = 16 * c < Dio * E::E;   // past the io row: the ring row's zero padding
+                const uint4 kk = in ? gld<uint4>((const char*)a.k + src) : make_uint4(0u, 0u, 0u, 0u);
+                const uint4 vv = in ? gld<uint4>((const char*)a.v + src) : make_uint4(0u, 0u, 0u, 0u);
                 gst<uint4>(kd, kk);
                 gst<uint4>(kd + a.g.v_off, vv);
             }
@@ -643,8 +662,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     // has read the old waiting rows before the barrier
     if constexpr (LOOK) {
         if (a.look_keep > 0 && qc == 0) {
-            const long long rowb = (long long)a.g.hq * D * E::E;
-            const int c0 = g0 * group * D * E::E / 16, nc = hg * group * D * E::E / 16;
+            const long long rowb = (long long)a.g.hq * Dio * E::E;
+            const int c0 = g0 * group * Dio * E::E / 16, nc = hg * group * Dio * E::E / 16;
             char* pend = (char*)t.ring[si] + a.pend_off + (long long)(m.layer0 + m.l_off + li) * a.pend_layer;
             const int p = a.look_pend, keep = a.look_keep, shift = p + m.n - keep;
             for (int c = threadIdx.x; c < nc; c += blockDim.x)
@@ -818,11 +837,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
                 } else {
                     const int hq = g * group + gh;
                     const long long orow = (LOOK ? (long long)a.look_o0 : (long long)m.t0) + (long long)qc * a.qchunk + j;
-                    char* dst = (char*)a.out + ((cu * m.n_total + orow) * a.g.hq + hq) * (long long)D * E::E;
+                    char* dst = (char*)a.out + ((cu * m.n_total + orow) * a.g.hq + hq) * (long long)Dio * E::E;
 #pragma unroll
                     for (int k = 0; k < DPL; ++k) {
                         const float o = acc[i][k] / lrow;
                         const int d = lane + 64 * k;
+                        if (kNarrow && d >= Dio) continue;   // a padding dim of the ring row
                         if constexpr (E::E == 2)
                             gst<uint16_t>(dst + 2 * d, (uint16_t)to_bf16(o));
                         else
@@ -1213,7 +1233,7 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
 template <class E, int D>
 __global__ __launch_bounds__(64) void k_pend_save(AttnArgs a, StateTable t, int keep) {
     const UnitMap& m = a.m;
-    const long long row = (long long)a.g.hq * D * E::E;
+    const long long row = (long long)a.g.hq * a.g.Dio * E::E;   // io rows
     const int nch = (int)(row / 16), bpu = (nch + 63) / 64;
     const int unit = blockIdx.x / bpu, c = (blockIdx.x - unit * bpu) * 64 + threadIdx.x;
     if (c >= nch) return;
@@ -1377,7 +1397,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t 
 
 hipError_t launch_pend_save(const AttnArgs& a, const StateTable& t, int keep, hipStream_t s) {
     if (keep < 1) return hipSuccess;
-    const long long row = (long long)a.g.hq * a.g.D * (a.g.dtype == 1 ? 2 : 4);
+    const long long row = (long long)a.g.hq * a.g.Dio * (a.g.dtype == 1 ? 2 : 4);
     const long long bpu = (row / 16 + 63) / 64;
     const dim3 grid((unsigned)((long long)a.m.n_states * a.m.nl * bpu));
     VRT_DISPATCH_ED(a.g.dtype, a.g.D, {

@@ -77,25 +77,30 @@ class Pool:
 
     def __init__(self, desc, n: int, starts):
         self.desc = desc
-        self.nbytes = vrt.state_device_bytes(desc)
+        nb = vrt.state_device_bytes(desc)
+        self.nbytes = (nb + 255) // 256 * 256      # state memory must be 256-byte aligned
         self.mem = torch.empty(n * self.nbytes, dtype=torch.uint8, device=DEV)
         self.states = [vrt.StreamState(desc, self.mem[i * self.nbytes:(i + 1) * self.nbytes],
-                                       self.nbytes, int(starts[i])) for i in range(n)]
+                                       nb, int(starts[i])) for i in range(n)]
+
+    def row_elems(self) -> int:
+        """Elements per ring row (a lookahead head narrower than 64 is padded)."""
+        return max(self.desc.head_dim, 64)
 
     def ring_rows(self, i: int, layer: int, which: int, head: int, s0: int, s1: int) -> np.ndarray:
         """Rows [s0, s1) of one ring slice, as float32 values."""
-        d = self.desc
+        d, r = self.desc, self.row_elems()
         e = 2 if d.dtype == vrt.BF16 else 4
         off = i * self.nbytes + vrt.ring_offset(d, layer, which, head)
-        raw = self.mem[off + s0 * d.head_dim * e: off + s1 * d.head_dim * e]
+        raw = self.mem[off + s0 * r * e: off + s1 * r * e]
         t = raw.view(torch.bfloat16 if e == 2 else torch.float32)
-        return t.float().cpu().numpy().reshape(s1 - s0, d.head_dim)
+        return t.float().cpu().numpy().reshape(s1 - s0, r)
 
     def ring_bytes(self, i: int, layer: int, which: int, head: int, s0: int, s1: int) -> bytes:
-        d = self.desc
+        d, r = self.desc, self.row_elems()
         e = 2 if d.dtype == vrt.BF16 else 4
         off = i * self.nbytes + vrt.ring_offset(d, layer, which, head)
-        return self.mem[off + s0 * d.head_dim * e: off + s1 * d.head_dim * e].cpu().numpy().tobytes()
+        return self.mem[off + s0 * r * e: off + s1 * r * e].cpu().numpy().tobytes()
 
     def close(self):
         for s in self.states:

@@ -49,6 +49,13 @@ def test_desc_checks():
     bad = vrt.enc_desc()
     bad.dtype = 7
     assert vrt.desc_check(bad) == vrt.ERR_UNSUPPORTED
+    # heads narrower than 64 only without rotation (the moonshine encoder's 8 x 40)
+    assert vrt.desc_check(vrt.lookahead_desc(16, 4, head_dim=40)) == vrt.OK
+    assert vrt.desc_check(vrt.lookahead_desc(16, 4, head_dim=8)) == vrt.OK
+    assert vrt.desc_check(vrt.lookahead_desc(16, 4, head_dim=36)) == vrt.ERR_UNSUPPORTED
+    assert vrt.desc_check(vrt.lookahead_desc(16, 4, head_dim=96)) == vrt.ERR_UNSUPPORTED
+    assert vrt.desc_check(vrt.enc_desc(head_dim=40)) == vrt.ERR_UNSUPPORTED
+    assert vrt.desc_check(vrt.dec_desc(head_dim=40)) == vrt.ERR_UNSUPPORTED
 
 
 def test_state_bytes_and_offsets():
@@ -62,6 +69,11 @@ def test_state_bytes_and_offsets():
     assert vrt.ring_offset(d, 3, 1, 5) == 3 * 40 * sl + 25 * sl
     assert vrt.ring_offset(d, 32, 0, 0) == 2 ** 64 - 1
     assert vrt.offline_scratch_bytes(d, 1000) == 2 * 20 * 1000 * 64 * 2
+    # a 40-wide lookahead head: ring rows padded to 64, waiting q rows 40 wide
+    la = vrt.lookahead_desc(16, 4, n_layers=6, head_dim=40)
+    assert vrt.state_device_bytes(la) == 6 * (2 * 8 * la.ring_slots * 64 * 2 + 3 * 8 * 40 * 2)
+    assert vrt.ring_offset(la, 1, 1, 2) == (2 * 8 * la.ring_slots * 64 * 2) + 10 * la.ring_slots * 64 * 2
+    assert vrt.offline_scratch_bytes(la, 100) == 2 * 8 * 100 * 64 * 2
 
 
 def test_ring_advance_matches_oracle_model():

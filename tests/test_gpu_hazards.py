@@ -113,15 +113,16 @@ def test_offline_reads_only_written_scratch(dtype, T):
     _both(run)
 
 
-def test_lookahead_reads_only_written_rows():
-    S, L, T, H, d = 2, 1, 600, 8, 64
-    desc = vrt.lookahead_desc(16, 4, n_layers=L)
+@pytest.mark.parametrize("d", [40, 64])
+def test_lookahead_reads_only_written_rows(d):
+    S, L, T, H = 2, 1, 600, 8
+    desc = vrt.lookahead_desc(16, 4, n_layers=L, head_dim=d)
     q, k, v = seqs(93, S, L, T, H, d, 1.0, vrt.BF16)
     qd, kd, vd = (to_dev(x, vrt.BF16) for x in (q, k, v))
 
     def run(byte):
         pool = _filled_pool(desc, S, [0, 0], byte)
-        say(f"lookahead (16, 4): state memory filled with {byte:#04x}")
+        say(f"lookahead (16, 4), head_dim {d}: state memory filled with {byte:#04x}")
         outs, t = [], 0
         for m in [1, 4, 7, 64, 3] * 100:
             if t >= T:

@@ -39,10 +39,13 @@ def _feed_all(pool, idx, L, qd, kd, vd, sizes):
     return host(torch.cat(outs, dim=2))
 
 
-@pytest.mark.parametrize("dtype,left,right", [(vrt.BF16, 16, 4), (vrt.F32, 16, 4), (vrt.BF16, 16, 0),
-                                              (vrt.BF16, 16, 1), (vrt.BF16, 100, 9)])
-def test_lookahead_chunkings_offline_and_oracle(dtype, left, right):
-    S, L, T, H, d = 2, 2, 300, 8, 64
+@pytest.mark.parametrize("dtype,left,right,d", [
+    (vrt.BF16, 16, 4, 40), (vrt.F32, 16, 4, 40), (vrt.BF16, 16, 0, 40), (vrt.BF16, 16, 1, 40),
+    (vrt.BF16, 100, 9, 40), (vrt.BF16, 16, 4, 64), (vrt.F32, 100, 9, 64), (vrt.BF16, 16, 4, 8)])
+def test_lookahead_chunkings_offline_and_oracle(dtype, left, right, d):
+    """8 heads of 40 is the moonshine streaming encoder's head (hidden 320);
+    heads narrower than 64 are stored in zero-padded 64-element ring rows."""
+    S, L, T, H = 2, 2, 300, 8
     f = max(right - 1, 0)
     desc = vrt.lookahead_desc(left, right, dtype=dtype, n_layers=L, heads=H, head_dim=d)
     q, k, v = seqs(90 + right, S, L, T, H, d, 1.0, dtype)
@@ -51,7 +54,7 @@ def test_lookahead_chunkings_offline_and_oracle(dtype, left, right):
     runs = {}
     for sizes in ([4], [1], [7], [64], [512]):
         pool = Pool(desc, S, starts)
-        say(f"lookahead ({left}, {right}): feeds {sizes}")
+        say(f"lookahead ({left}, {right}), {H} x {d}: feeds {sizes}")
         runs[sizes[0]] = _feed_all(pool, range(S), L, qd, kd, vd, sizes)
         for s in range(S):
             assert pool.states[s].query(0) == (starts[s], T)
