@@ -773,7 +773,9 @@ BLOCK_KERNELS = ("k_gemm_qkv", "k_gemm_o", "k_rmsnorm", "k_gemm_conv", "k_gemm_r
 
 
 def kernel_source(kernel: str) -> str:
-    return os.path.join(KERNEL_DIR, "vrt_block.hip" if kernel in BLOCK_KERNELS else "vrt_kernels.hip")
+    if kernel in BLOCK_KERNELS:
+        return os.path.join(KERNEL_DIR, "vrt_block.hip")
+    return os.path.join(KERNEL_DIR, "vrt_mfma.hip" if kernel == "k_attn_mfma" else "vrt_kernels.hip")
 
 
 def source_sha256(path: str) -> str:
@@ -934,7 +936,7 @@ def bench_c1(args):
     # the same kind of step as 32 per-layer calls of 64 streams each (the
     # order in which a real encoder runs its layers: one layer's output is the
     # next one's input), on the wall clock, continuing the same streams
-    nl_steps = min(args.steps, 50)
+    nl_steps = min(args.steps, max(0, args.per_layer_steps))
     Qp, Kp, Vp = (x[args.warmup:args.warmup + nl_steps].transpose(1, 2).contiguous() for x in (Q, K, V))
     out_l = torch.empty((S, 1, n, H, D), dtype=torch.bfloat16, device=dev)
     log(f"c1: timing {nl_steps} steps as {L} per-layer calls each")
@@ -944,7 +946,7 @@ def bench_c1(args):
         for l in range(L):
             vrt.enc_attn_feed(states, l, 1, Qp[j, l], Kp[j, l], Vp[j, l], n, out_l, stream)
     torch.cuda.synchronize()
-    wall_l = time.perf_counter() - t1
+    wall_l = max(time.perf_counter() - t1, 1e-9)
     del Qp, Kp, Vp
     for st in states:
         st.close()
@@ -985,7 +987,7 @@ def bench_c1(args):
             "launches_timed": len(attn_ms),
         },
         "step_hbm_frac": sum(nbytes) / wall / 1e9 / HBM_PEAK_GBS,
-        "per_layer_calls": {
+        "per_layer_calls": None if nl_steps == 0 else {
             "steps": nl_steps, "ms_per_step": wall_l * 1e3 / nl_steps,
             "value": S * n * nl_steps / wall_l,
             "note": "each step as 32 calls (one layer of all 64 streams each, 64 units per launch), "
@@ -1270,6 +1272,9 @@ def main():
     ap.add_argument("--device-warmup", type=float, default=DEVICE_WARMUP_S,
                     help="seconds of untimed HBM streaming before the warmup steps (0: none; "
                          "profiler runs use 0 to keep the trace small)")
+    ap.add_argument("--per-layer-steps", type=int, default=50,
+                    help="c1: also time this many steps as 32 per-layer calls (0: skip; "
+                         "profiler runs skip them)")
     ap.add_argument("--ring", default="compact", choices=["compact", "mod"],
                     help="encoder configs: compacting ring (the pages') or modulo ring")
     ap.add_argument("--timing-every", type=int, default=None,

@@ -19,9 +19,9 @@
 //                  result does not depend on which other queries share its
 //                  workgroup, on ring slots or on compaction: chunked feeding
 //                  reproduces the offline pass bit for bit.
-//   k_attn_mfma    the same attention for sub-batches of 32 or more bf16
-//                  frames (the catch-up path), with both products on the
-//                  matrix cores and the same absolute tile grid.
+//   k_attn_mfma    (vrt_mfma.hip) the same attention for sub-batches of 32 or
+//                  more bf16 frames (the catch-up path), with both products
+//                  on the matrix cores and the same absolute tile grid.
 //   k_dec_combine  log-sum-exp merge of split-K partials in ascending split
 //                  order (decode step).
 //
@@ -34,167 +34,11 @@
 #include <algorithm>
 #include <mutex>
 
+#include "vrt_device.h"
 #include "vrt_internal.h"
 
 namespace vrt {
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-struct F32T { static constexpr int E = 4; };
-struct BF16T { static constexpr int E = 2; };
-
-// Global-memory accesses go through address-space-1 pointers: the ring and
-// I/O addresses arrive as integers in the kernel arguments, and through a
-// generic pointer the compiler would emit flat loads, which also count on the
-// LDS wait counter and so make every LDS wait in the tile loop wait for the
-// next tiles' HBM loads too.
-#define VRT_GLOBAL __attribute__((address_space(1)))
-template <int B> struct Raw;
-template <> struct Raw<2> { typedef unsigned short T; };
-template <> struct Raw<4> { typedef unsigned int T; };
-template <> struct Raw<8> { typedef unsigned int T __attribute__((ext_vector_type(2))); };
-template <> struct Raw<16> { typedef unsigned int T __attribute__((ext_vector_type(4))); };
-template <class T>
-__device__ __forceinline__ T gld(const void* p) {
-    typedef typename Raw<sizeof(T)>::T R;
-    const R r = *(const VRT_GLOBAL R*)(__UINTPTR_TYPE__)p;
-    return __builtin_bit_cast(T, r);
-}
-template <class T>
-__device__ __forceinline__ void gst(void* p, T v) {
-    typedef typename Raw<sizeof(T)>::T R;
-    *(VRT_GLOBAL R*)(__UINTPTR_TYPE__)p = __builtin_bit_cast(R, v);
-}
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
-__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ long long floor_div(long long a, long long b) {
-    long long q = a / b;
-    return (a % b != 0 && (a < 0)) ? q - 1 : q;
-}
-
-// ---------------------------------------------------------------- RoPE ----
-// angle = pos * omega_i in fp64 (a float32 angle is off by up to ~0.03 rad at
-// positions near 1e6); omega_i = theta^(-2i/D) comes from the host in fp64.
-// The angle is first reduced by multiples of 2*pi with the additive method of
-// Cody and Waite (1980): 2*pi is split into three doubles, the first two with
-// 30 significant bits, so k*c1 and k*c2 are exact for |k| < 2^23 and the three
-// fused steps leave the reduced angle accurate to about one ulp.  sincos then
-// runs on an argument in [-pi, pi]; beyond |x| = 2.6e7 the library reduces it.
-__device__ __forceinline__ void rope_angle(long long pos, double omega, double* c, double* s) {
-    double x = (double)pos * omega;
-    if (fabs(x) < 2.6e7) {
-        const double k = rint(x * 0.15915494309189535);  // x / (2 pi), nearest integer
-        x = fma(-k, 6.283185303211212, x);
-        x = fma(-k, 3.9683743166540886e-09, x);
-        x = fma(-k, 2.068073192717642e-18, x);
-    }
-    sincos(x, s, c);
-}
-
-// NEOX pair (i, i + D/2): y0 = x0 cos - x1 sin, y1 = x1 cos + x0 sin, in fp64,
-// rounded once to fp32.
-__device__ __forceinline__ void rope_rot(float x0, float x1, double c, double s, float* y0,
-                                         float* y1) {
-    const double a = (double)x0 * c;
-    const double b = (double)x1 * s;
-    const double e = (double)x1 * c;
-    const double f = (double)x0 * s;
-    *y0 = (float)(a - b);
-    *y1 = (float)(e + f);
-}
-
-// (cos, sin) of a rotation angle x = p * omega_i, 0 <= p < 2^31.  The
-// fp64 angle is reduced by 2 pi with a four-part Cody-Waite split whose first
-// three parts have 24 significant bits, so k * c_j is exact for |k| < 2^29
-// (every angle below 3.3e9 rad, which covers all positions the library
-// accepts) and the reduced angle is accurate to about 1e-15 rad; the
-// hardware sine / cosine then run on it in revolutions (1.2e-7 abs. error).
-struct CosSin { float c, s; };
-__device__ __forceinline__ CosSin rope_cs(double x) {
-    const double k = rint(x * 0x1.45f306dc9c883p-3);      // x / (2 pi)
-    x = fma(-k, 0x1.921fb60000000p+2, x);
-    x = fma(-k, -0x1.777a5c0000000p-23, x);
-    x = fma(-k, -0x1.ee59da0000000p-48, x);
-    x = fma(-k, 0x1.98a2e03707345p-75, x);
-    const float r = (float)(x * 0x1.45f306dc9c883p-3);
-    return CosSin{__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r)};
-}
-
-// One NEOX rotation per storage type.  fp32 storage: fp64 sin / cos and an
-// fp64 rotation rounded once to fp32 (rope_angle, rope_rot).  bf16 storage:
-// the exactly reduced angle and the hardware sine / cosine (rope_cs) and an
-// fp32 rotation; its error (~1e-7 of the values) is far below the bf16
-// rounding of the result.  Keys are written by one function per storage
-// type whichever kernel appends them, so ring contents do not depend on the
-// path that wrote them.
-template <class E> struct Angle;
-template <> struct Angle<F32T> { double c, s; };
-template <> struct Angle<BF16T> { float c, s; };
-template <class E> __device__ __forceinline__ Angle<E> rope_of(long long pos, double omega);
-template <> __device__ __forceinline__ Angle<F32T> rope_of<F32T>(long long pos, double omega) {
-    Angle<F32T> a;
-    rope_angle(pos, omega, &a.c, &a.s);
-    return a;
-}
-template <> __device__ __forceinline__ Angle<BF16T> rope_of<BF16T>(long long pos, double omega) {
-    const CosSin r = rope_cs((double)pos * omega);
-    return Angle<BF16T>{r.c, r.s};
-}
-__device__ __forceinline__ void rope_pair(float x0, float x1, Angle<F32T> a, float* y0, float* y1) {
-    rope_rot(x0, x1, a.c, a.s, y0, y1);
-}
-__device__ __forceinline__ void rope_pair(float x0, float x1, Angle<BF16T> a, float* y0, float* y1) {
-    *y0 = __fmaf_rn(x0, a.c, -(x1 * a.s));
-    *y1 = __fmaf_rn(x1, a.c, x0 * a.s);
-}
-
-template <class E> __device__ __forceinline__ void ld4(const char* p, float (&x)[4]);
-template <> __device__ __forceinline__ void ld4<F32T>(const char* p, float (&x)[4]) {
-    const float4 v = gld<float4>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
-template <> __device__ __forceinline__ void ld4<BF16T>(const char* p, float (&x)[4]) {
-    const uint2 v = gld<uint2>(p);
-    x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
-}
-// Four consecutive elements in the storage type; G: global memory, else LDS.
-template <class E, bool G> __device__ __forceinline__ void st4(char* p, const float (&x)[4]);
-template <> __device__ __forceinline__ void st4<F32T, true>(char* p, const float (&x)[4]) {
-    gst<float4>(p, make_float4(x[0], x[1], x[2], x[3]));
-}
-template <> __device__ __forceinline__ void st4<F32T, false>(char* p, const float (&x)[4]) {
-    *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
-}
-__device__ __forceinline__ uint2 pack_bf16x4(const float (&x)[4]) {
-    uint2 v;
-    v.x = to_bf16(x[0]) | (to_bf16(x[1]) << 16);
-    v.y = to_bf16(x[2]) | (to_bf16(x[3]) << 16);
-    return v;
-}
-template <> __device__ __forceinline__ void st4<BF16T, true>(char* p, const float (&x)[4]) {
-    gst<uint2>(p, pack_bf16x4(x));
-}
-template <> __device__ __forceinline__ void st4<BF16T, false>(char* p, const float (&x)[4]) {
-    *(uint2*)p = pack_bf16x4(x);
-}
 
 // ---------------------------------------------------------- K1: append ----
 // One workgroup per (unit, group of 4 frames).  Each thread rotates 4 NEOX
@@ -360,76 +204,6 @@ struct Tl {
     static constexpr int QCAP = kQsBytes;        // rotated query rows of the head group
     static constexpr int BYTES = NST * 2 * TILE + QCAP + 4 * PRB;
 };
-template <int CPR>
-__device__ __forceinline__ int ksw(int r) { return CPR == 8 ? ((r >> 1) & 7) : (r & 15); }
-// V rows: a transposing read covers 4 consecutive rows; XOR the chunk index so
-// those 4 rows fall on distinct banks (128-byte rows pair up as r, r+2; 256-byte
-// rows all start on bank 0).
-template <class E, int CPR>
-__device__ __forceinline__ int vsw(int r) {
-    if constexpr (E::E == 4) return 0;
-    return CPR == 8 ? (((r >> 1) & 1) << 2) : ((r & 3) << 2);
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-#define VRT_LDS __attribute__((address_space(3)))
-
-// 16 bytes per lane, HBM -> LDS (global_load_lds_dwordx4: lane i writes
-// bytes [16i, 16i + 16) after the wave-uniform LDS address in M0).  Issued
-// through inline asm on purpose: the compiler does not track LDS writes
-// made this way, so it does not make every later LDS read of the tile loop
-// wait for the DMA of the tile being prefetched.  Every read of a stage is
-// ordered after its DMA explicitly (wait_vm, then a workgroup barrier).
-// Untracked vector-memory operations can only make the compiler's own
-// vmcnt waits stricter, never weaker.
-// M0 is saved and restored around the instruction (the compiler reserves
-// it), with the one wait state an M0 write needs before an LDS DMA.
-// The loads carry the non-temporal hint: the vector kernel reads each window
-// row once per launch, and streaming them past the caches' retention raised
-// the serving step from 66.8 % to 69.9 % and the decode step from 68.3 % to
-// 76.1 % of peak HBM bandwidth (measured back to back on one MI355X).
-__device__ __forceinline__ void dma16(const char* g, char* l) {
-    const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(__UINTPTR_TYPE__)l);
-    unsigned saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off nt\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"((unsigned long long)(__UINTPTR_TYPE__)g), "s"(lds)
-        : "memory");
-}
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
-// byte offset (global_load_lds with saddr): no 64-bit address per lane.
-__device__ __forceinline__ void dma16s(const char* base, unsigned off, char* l) {
-    const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(__UINTPTR_TYPE__)l);
-    unsigned saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(off), "s"(base), "s"(lds)
-        : "memory");
-}
-// lane id read through volatile asm: recomputed where used instead of being
-// kept live (or spilled) across a loop
-__device__ __forceinline__ int lane_id_v() {
-    int l;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-    return l;
-}
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // RPW: rows per wave (1 when a head has at most 4 rows; then the wave's query
 // row of the current head is kept in registers for that head's key loop).
 // LOOK: (left, right) windows without rotation (moonshine streaming encoder):
@@ -854,377 +628,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     }
 }
 
-// ------------------------------------------------ K4: attention, MFMA ----
-// The same windowed-causal attention for large sub-batches (the catch-up
-// path): bf16 storage, head_dim 64, one query head per kv head.  One
-// workgroup of 4 waves per (unit, head, tile of 128 queries); wave w owns
-// queries 32w .. 32w+31 of the tile.  Both products run on the bf16 matrix
-// cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation) in transposed form:
-//   S^T = K Q^T      (32 keys x 32 queries per block; lane = query, so the
-//                    softmax of a query is local to the lane and its partner
-//                    lane in the other half of the wave)
-//   O^T += V^T P^T   (32 dims x 32 queries; V^T is read from LDS with the
-//                    transposing read, P^T is S^T's registers, packed)
-// With the MFMA result layout (lane l, register r: key 8(r/4) + 4(l/32) +
-// r%4 of the block, query l%32), registers 8c .. 8c+7 of a lane hold the
-// eight keys that lane contributes to the k = 16 product of key group c; the
-// V^T operand is read with the same key order.
-//
-// Keys stream through LDS in 64-key tiles aligned to absolute position (the
-// same tiles and clamped-row fetch as the VALU kernel); a 32-key half-tile
-// outside the band of all 32 queries of a wave is skipped, which is exact:
-// such a half-tile would only add zero weights.  The softmax scale is folded
-// into the rotated query, so scores come out in log2 units, and the matrix
-// cores also subtract a per-query reference maximum (an extra k-step), which
-// moves only when a half-tile's scores exceed it by more than 2^8 (then the
-// accumulators are rescaled), so most half-tiles need neither a subtraction
-// nor a rescale on the vector ALU.  The denominator sums the bf16 weights the products use.
-// Every per-query step (the MFMA chains, the reference, the partial sums,
-// the rescale) depends only on that query's own window and the absolute tile
-// grid, so the result does not depend on how frames were batched.
-//
-// Queries are rotated in the prologue: the angle p * omega_i is formed and
-// reduced by 2 pi in fp64 as for the keys, then sin and cos are taken in fp32
-// on the reduced angle (error ~3e-7 rad, far below the bf16 rounding of the
-// rotated, scaled query that follows).
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-struct M4 {
-    static constexpr int D = 64;
-    static constexpr int RB = 128;                // bytes per K / V row
-    static constexpr int CPR = 8;                 // 16-byte chunks per row
-    static constexpr int QW = 32;                 // queries per wave
-    static constexpr int QT = 4 * QW;             // queries per workgroup
-    static constexpr int TILE = kTile * RB;       // 8 KB
-    static constexpr int NST = 2;                 // LDS stages (4 workgroups per CU fit)
-    static constexpr int IPW = TILE / (4 * 1024); // DMA instructions per wave per K (or V) tile
-    static constexpr int LPW = 2 * IPW;
-    static constexpr int BYTES = NST * 2 * TILE;
-};
-static_assert(M4::QT == kQTileMfma, "query tile of the MFMA path");
-static_assert(M4::NST == 2, "the tile loop's DMA waits assume two stages");
-// A query's reference maximum moves only when a half-tile's scores exceed it
-// by more than this (log2 units), so unnormalised weights stay below 2^8.
-constexpr float kLazy = 8.0f;
-
-// max(a, b, c); the compiler folds the pair into one v_max3_f32.  Written
-// with builtins, not inline asm, on purpose: the operands are often matrix-core
-// results, and only compiler-visible reads get the wait states the hardware
-// requires between an MFMA writing a register and a VALU reading it.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    const b2 v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// At most 128 VGPRs (four waves per SIMD), so four workgroups share a CU; the
-// tile loop works on one 32-key half-tile at a time to stay within them.
-__global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) {
-    using L = M4;
-    __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int jq = lane & 31;        // query of the lane within the wave
-    const int hf = lane >> 5;        // half of the wave
-
-    // Workgroup -> (unit, head, query tile).  Workgroups are dispatched to the
-    // 8 XCDs round robin; consecutive logical ids (the query tiles of one
-    // (unit, head), which read overlapping key windows) are placed on the same
-    // XCD so its L2 serves the overlap.
-    int b;
-    {
-        const int nb = gridDim.x, x = blockIdx.x & 7, s = blockIdx.x >> 3;
-        const int base = nb >> 3, rem = nb & 7;
-        b = x < rem ? x * (base + 1) + s : rem * (base + 1) + (x - rem) * base + s;
-    }
-    const int qc = b % a.n_qchunks;
-    b /= a.n_qchunks;
-    const int g = b % a.g.hkv;
-    const int unit = b / a.g.hkv;
-    const UnitMap& m = a.m;
-    const int si = unit / m.nl, li = unit - si * m.nl;
-    const long long cu = (long long)t.call_idx[si] * m.nl_call + m.l_off + li;
-
-    const int W = a.g.window;
-    const long long avail = t.p0[si] - t.n_kv[si];
-    const long long pq0 = t.p0[si] + (long long)qc * L::QT;
-    const int nq = min(L::QT, m.n - qc * L::QT);
-    const long long wlo = max(avail, pq0 - W + 1);
-    const long long whi = pq0 + nq - 1;
-    const long long tfirst = floor_div(wlo, kTile);
-    const int ntt = (int)(floor_div(whi, kTile) - tfirst + 1);
-    const long long T0 = tfirst * kTile;
-
-    char* layer = (char*)t.ring[si] + (long long)(m.layer0 + m.l_off + li) * a.g.layer_bytes;
-    const char* Kg = layer + (long long)g * a.g.slice_bytes;
-    const char* Vg = Kg + a.g.v_off;
-
-    // the lane's 16-byte chunk of each DMA instruction: tile row r and its
-    // swizzled byte offset; kept for the tiles whose rows are all in range
-    unsigned dk[L::IPW], dv[L::IPW];
-#pragma unroll
-    for (int i = 0; i < L::IPW; ++i) {
-        const int q = (wave * L::IPW + i) * 64 + lane;
-        const int r = q / L::CPR, pc = q % L::CPR;
-        dk[i] = (unsigned)r * L::RB + 16 * (pc ^ ksw<L::CPR>(r));
-        dv[i] = (unsigned)r * L::RB + 16 * (pc ^ vsw<BF16T, L::CPR>(r));
-    }
-    auto issue = [&](int T, int st) {
-        const long long TB = T0 + (long long)T * kTile;
-        // modulo ring: 0 <= TB < 2^31 and the slot count is a multiple of 64,
-        // so a tile is contiguous in the ring and 32-bit arithmetic is exact
-        const long long sb = a.g.mod ? (long long)((unsigned)TB % (unsigned)a.g.slots) : TB - avail;
-        const int rlo = (int)max(0LL, wlo - TB), rhi = (int)min(63LL, whi - TB);
-        char* ks = lds + st * 2 * L::TILE;
-        char* vs = ks + L::TILE;
-        if (rlo == 0 && rhi == 63) {
-#pragma unroll
-            for (int i = 0; i < L::IPW; ++i) {
-                const int ins = wave * L::IPW + i;
-                dma16s(Kg + sb * L::RB, dk[i], ks + ins * 1024);
-                dma16s(Vg + sb * L::RB, dv[i], vs + ins * 1024);
-            }
-            return;
-        }
-        // an edge tile: rows outside [rlo, rhi] repeat the nearest row in range
-#pragma unroll
-        for (int i = 0; i < L::IPW; ++i) {
-            const int ins = wave * L::IPW + i;
-            const int q = ins * 64 + lane_id_v();
-            const int r = q / L::CPR, pc = q % L::CPR;
-            const int rr = min(max(r, rlo), rhi);
-            const unsigned off = (unsigned)rr * L::RB;
-            dma16s(Kg + sb * L::RB, off + 16 * (pc ^ ksw<L::CPR>(r)), ks + ins * 1024);
-            dma16s(Vg + sb * L::RB, off + 16 * (pc ^ vsw<BF16T, L::CPR>(r)), vs + ins * 1024);
-        }
-    };
-
-    // ---- this wave's queries; lanes past the last query repeat it
-    const int qw0 = wave * L::QW;
-    const int nqw = min(L::QW, nq - qw0);   // may be <= 0 for the last tile
-    const int jj = max(0, min(jq, nqw - 1));
-    const long long pq = pq0 + qw0 + jj;
-    const long long frame = m.t0 + (long long)qc * L::QT + qw0 + jj;
-    const char* qsrc =
-        (const char*)a.q + ((cu * m.n_total + frame) * a.g.hq + g) * (long long)(L::D * 2);
-    uint4 qraw[4];
-    double om[16];
-    if (nqw > 0) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qraw[s] = gld<uint4>(qsrc + 32 * s + 16 * hf);
-        const double* wp = a.g.omega + 8 * hf;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) om[8 * s + e] = wp[16 * s + e];
-    }
-#pragma unroll
-    for (int st = 0; st < L::NST - 1; ++st)
-        if (st < ntt) issue(st, st);
-
-    // rotate: the lane holds dims 16s + 8hf + e (s = 0..3, e = 0..7); NEOX
-    // pairs (i, i + 32) are chunks s and s + 2 of the same lane.
-    bf16x8_t qt[4];
-    const float qscale = a.scale_log2;   // scores come out in log2 units
-    if (nqw > 0) {
-        float cs[16], sn[16];
-        const double pd = (double)pq;
-        // frequencies 16s + 8hf + e: two contiguous runs of 8 doubles of
-        // the argument block per lane, loaded up front
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const CosSin r = rope_cs(pd * om[i]);
-            cs[i] = r.c;
-            sn[i] = r.s;
-        }
-        wait_vm<L::LPW>();   // the query loads (only tile 0 was issued after them)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint32_t* x0 = (const uint32_t*)&qraw[s];
-            const uint32_t* x1 = (const uint32_t*)&qraw[s + 2];
-            uint32_t y0[4], y1[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                float a0[2], a1[2], b0[2], b1[2];
-                a0[0] = bf_lo(x0[w]); a0[1] = bf_hi(x0[w]);
-                a1[0] = bf_lo(x1[w]); a1[1] = bf_hi(x1[w]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const float c = cs[8 * s + 2 * w + u], sv = sn[8 * s + 2 * w + u];
-                    b0[u] = __fmaf_rn(a0[u], c, -(a1[u] * sv)) * qscale;
-                    b1[u] = __fmaf_rn(a1[u], c, a0[u] * sv) * qscale;
-                }
-                y0[w] = pack_bf16x2(b0[0], b0[1]);
-                y1[w] = pack_bf16x2(b1[0], b1[1]);
-            }
-            qt[s] = __builtin_bit_cast(bf16x8_t, make_uint4(y0[0], y0[1], y0[2], y0[3]));
-            qt[s + 2] = __builtin_bit_cast(bf16x8_t, make_uint4(y1[0], y1[1], y1[2], y1[3]));
-        }
-    }
-
-    // ---- bands relative to T0: the lane's query, and the wave's union /
-    // intersection (for skipping and for mask-free half-tiles)
-    // the lane's own band [max(alo, h - W + 1), h] with h = hq0 + its query
-    // index is recomputed on the edge half-tiles that need it
-    const int hq0 = (int)(pq0 + qw0 - T0), alo = (int)(avail - T0);
-    const long long wq_first = pq0 + qw0, wq_last = pq0 + qw0 + max(nqw, 1) - 1;
-    const int blo = (int)(max(avail, wq_first - W + 1) - T0), bhi = (int)(wq_last - T0);
-    const int flo = (int)(max(avail, wq_last - W + 1) - T0), fhi = (int)(wq_first - T0);
-
-    f32x16_t o[2];
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-    // Reference maximum of the lane's query (log2 units), subtracted from the
-    // scores by the matrix cores themselves: a fifth k-step per score block
-    // multiplies the constant operand kext (ones at k = 0, 1) with qext =
-    // (-m_hi, -m_lo), the reference split into two bf16 values, so the block
-    // comes out as s - mref with mref = m_hi + m_lo exactly.  mref is 0 until
-    // the query's first visible key, then moves only when a half-tile's maximum
-    // exceeds it by more than kLazy (weights stay below 2^kLazy); a lane whose
-    // reference does not move is rescaled by exactly 1, if at all.
-    // lane parts of the LDS addresses (the swizzles depend only on lane
-    // bits, so each read is a stage base + one of these + an immediate)
-    int koff[4], voff[2];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) koff[st] = jq * L::RB + 16 * ((2 * st + hf) ^ ksw<L::CPR>(jq));
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        const int row = 4 * hf + ((lane & 15) >> 2);
-        const int byte = 2 * (32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-        voff[d] = L::TILE + row * L::RB + 16 * ((byte >> 4) ^ vsw<BF16T, L::CPR>(row)) + (byte & 15);
-    }
-    const uint32_t one_lo = hf == 0 ? 0x3f803f80u : 0u;
-    const bf16x8_t kext = __builtin_bit_cast(bf16x8_t, make_uint4(one_lo, 0u, 0u, 0u));
-    bf16x8_t qext = __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
-    float mref = 0.f, lpart = 0.f;
-    bool seen = false;
-    constexpr uint32_t kOnes = 0x3f803f80u;   // (1, 1) in bf16
-
-    for (int T = 0; T < ntt; ++T) {
-        wait_vm<0>();   // two stages: only tile T is in flight here
-        __syncthreads();
-        if (T + L::NST - 1 < ntt) issue(T + L::NST - 1, (T + L::NST - 1) % L::NST);
-        const char* Sb = lds + (T % L::NST) * 2 * L::TILE;   // K tile, then V tile
-        const int tb = T * kTile;
-        if (nqw <= 0 || tb + 63 < blo || tb > bhi) continue;   // no key of this tile for the wave
-        bool rel[2], full[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int kb = tb + 32 * k;
-            rel[k] = kb + 31 >= blo && kb <= bhi;
-            full[k] = kb >= flo && kb + 31 <= fhi;
-        }
-        // one 32-key half-tile at a time: scores, reference update, weights,
-        // then its share of the output
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (!rel[k]) continue;
-            // scores relative to the reference: S^T = [K | 1] [Q | -mref]^T
-            bf16x8_t kv[4];
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                kv[st] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(Sb + koff[st] + 32 * k * L::RB));
-            f32x16_t s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, f32x16_t{}, 0, 0, 0);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[st], qt[st], s, 0, 0, 0);
-            // band mask on edge half-tiles (masked scores become the sentinel,
-            // whose weight underflows to exactly 0)
-            if (!full[k]) {
-                const int bhi_v = hq0 + min(lane_id_v() & 31, nqw - 1);
-                const int blo_v = max(alo, bhi_v - W + 1);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = tb + 32 * k + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    s[r] = (key >= blo_v && key <= bhi_v) ? s[r] : kSent;
-                }
-            }
-            float mt = kSent;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) mt = max3f(mt, s[r], s[r + 1]);
-            {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                                 false, false);
-                mt = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), kSent);
-            }
-            const bool move = seen ? mt > kLazy : mt > kSent;
-            if (__builtin_amdgcn_ballot_w64(move) != 0) {   // a query's first keys, or a jump of 2^kLazy
-                float delta = 0.f;
-                if (move) {
-                    const float mnew = mref + mt;
-                    const uint32_t hi = to_bf16(mnew);
-                    const float mhi = __uint_as_float(hi << 16);
-                    const uint32_t lo = to_bf16(mnew - mhi);
-                    const float mt_ref = mhi + __uint_as_float(lo << 16);
-                    const float alpha = seen ? fast_exp2(mref - mt_ref) : 0.f;
-                    lpart *= alpha;
-#pragma unroll
-                    for (int d = 0; d < 2; ++d)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-                    delta = mt_ref - mref;
-                    mref = mt_ref;
-                    seen = true;
-                    const uint32_t neg = (hi ^ 0x8000u) | ((lo ^ 0x8000u) << 16);
-                    qext = __builtin_bit_cast(bf16x8_t, make_uint4(hf == 0 ? neg : 0u, 0u, 0u, 0u));
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[r] -= delta;
-            }
-            uint32_t pb[8];
-#pragma unroll
-            for (int w = 0; w < 8; ++w) pb[w] = pack_bf16x2(fast_exp2(s[2 * w]), fast_exp2(s[2 * w + 1]));
-            // the denominator sums the same bf16 weights the products use
-#pragma unroll
-            for (int w = 0; w < 8; ++w) lpart = dot2bf(pb[w], kOnes, lpart);
-            // O^T += V^T P^T, key groups in ascending order
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const bf16x8_t pv = __builtin_bit_cast(
-                    bf16x8_t, make_uint4(pb[4 * c], pb[4 * c + 1], pb[4 * c + 2], pb[4 * c + 3]));
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    v4i16 part[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        part[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VRT_LDS v4i16*)(__UINTPTR_TYPE__)(
-                            Sb + voff[d] + (32 * k + 16 * c + 8 * u) * L::RB));
-                    const v8i16 vv = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pv,
-                                                                   o[d], 0, 0, 0);
-                }
-            }
-        }
-    }
-
-    // ---- epilogue: denominator = lower-half partial + upper-half partial
-    if (nqw <= 0) return;
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart), __float_as_uint(lpart),
-                                                     false, false);
-    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (jq >= nqw) return;
-    // one reciprocal per query instead of 32 divisions (the outputs are
-    // rounded to bf16 right after)
-    const float rl = 1.0f / l;
-    char* dst = (char*)a.out + ((cu * m.n_total + frame) * a.g.hq + g) * (long long)(L::D * 2);
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            uint2 v;
-            v.x = pack_bf16x2(o[d][4 * q4] * rl, o[d][4 * q4 + 1] * rl);
-            v.y = pack_bf16x2(o[d][4 * q4 + 2] * rl, o[d][4 * q4 + 3] * rl);
-            gst<uint2>(dst + 2 * (32 * d + 8 * q4 + 4 * hf), v);
-        }
-}
-
 // ------------------------------------------ waiting rows (lookahead) ----
 // One thread per 16-byte column of a q row: the last `keep` rows of [the
 // waiting rows | this sub-batch's q rows] move to the front of the waiting
@@ -1387,13 +790,6 @@ hipError_t launch_attn_valu(const AttnArgs& a, const StateTable& t, hipStream_t 
     return hipSuccess;
 }
 
-hipError_t launch_attn_mfma(const AttnArgs& a, const StateTable& t, hipStream_t s) {
-    if (a.g.dtype != 1 || a.g.D != 64 || a.g.group != 1 || a.n_splits != 1)
-        return hipErrorInvalidValue;
-    const long long blocks = (long long)a.m.n_states * a.m.nl * a.g.hkv * a.n_qchunks;
-    VRT_LAUNCH(k_attn_mfma, dim3((unsigned)blocks), dim3(256), 0, s, a, t);
-    return hipSuccess;
-}
 
 hipError_t launch_pend_save(const AttnArgs& a, const StateTable& t, int keep, hipStream_t s) {
     if (keep < 1) return hipSuccess;
