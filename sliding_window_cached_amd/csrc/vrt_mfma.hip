@@ -44,10 +44,12 @@ namespace {
 // the rescale) depends only on that query's own window and the absolute tile
 // grid, so the result does not depend on how frames were batched.
 //
-// Queries are rotated in the prologue: the angle p * omega_i is formed and
-// reduced by 2 pi in fp64 as for the keys, then sin and cos are taken in fp32
-// on the reduced angle (error ~3e-7 rad, far below the bf16 rounding of the
-// rotated, scaled query that follows).
+// Queries are rotated in the prologue: the angle p * omega_i is formed in
+// fp64 in revolutions and reduced to [-1/2, 1/2] there (three roundings of at
+// most 2^-53 relative each: below 1.2e-7 revolutions for every position under
+// 2^31), then sin and cos are taken in fp32 on the reduced angle (error below
+// 1e-6 rad in all, far below the bf16 rounding of the rotated, scaled query
+// that follows).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -200,9 +202,11 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
         // the argument block per lane, loaded up front
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const CosSin r = rope_cs(pd * om[i]);
-            cs[i] = r.c;
-            sn[i] = r.s;
+            // the angle in revolutions, reduced to [-1/2, 1/2]
+            const double x = (pd * om[i]) * 0x1.45f306dc9c883p-3;
+            const float r = (float)(x - rint(x));
+            cs[i] = __builtin_amdgcn_cosf(r);
+            sn[i] = __builtin_amdgcn_sinf(r);
         }
         wait_vm<L::LPW>();   // the query loads (only tile 0 was issued after them)
 #pragma unroll
@@ -229,14 +233,16 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
         }
     }
 
-    // ---- bands relative to T0: the lane's query, and the wave's union /
-    // intersection (for skipping and for mask-free half-tiles)
-    // the lane's own band [max(alo, h - W + 1), h] with h = hq0 + its query
-    // index is recomputed on the edge half-tiles that need it
+    // ---- bands relative to T0: the wave's union / intersection (for
+    // skipping and for mask-free half-tiles), and the lane's own band
+    // [max(alo, h - W + 1), h] with h the position of its query (lanes past
+    // the last query repeat it), for the edge half-tiles
     const int hq0 = (int)(pq0 + qw0 - T0), alo = (int)(avail - T0);
     const long long wq_first = pq0 + qw0, wq_last = pq0 + qw0 + max(nqw, 1) - 1;
     const int blo = (int)(max(avail, wq_first - W + 1) - T0), bhi = (int)(wq_last - T0);
     const int flo = (int)(max(avail, wq_last - W + 1) - T0), fhi = (int)(wq_first - T0);
+    const int bhi_v = hq0 + jj;
+    const int blo_v = max(alo, bhi_v - W + 1);
 
     f32x16_t o[2];
 #pragma unroll
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
     f32x4_t den = {0.f, 0.f, 0.f, 0.f};
     float mref = 0.f;
-    bool seen = false;
+    float thr = kSent;   // the reference moves when a half-tile's maximum exceeds it
 
     for (int T = 0; T < ntt; ++T) {
         wait_vm<0>();   // two stages: only tile T is in flight here
@@ -310,12 +316,20 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
             // band mask on edge half-tiles (masked scores become the sentinel,
             // whose weight underflows to exactly 0)
             if (!full[k]) {
-                const int bhi_v = hq0 + min(lane_id_v() & 31, nqw - 1);
-                const int blo_v = max(alo, bhi_v - W + 1);
+                // register r holds key tb + 32k + 4hf + c with c = 8(r/4) + r%4:
+                // bit c of vis says whether that key is in the query's band
+                const int lo = blo_v - (tb + 32 * k + 4 * hf), hi = bhi_v - (tb + 32 * k + 4 * hf);
+                const int lo_c = min(max(lo, 0), 31), hi_c = min(hi + 1, 28);
+                const int width = max(hi_c - lo_c, 0);
+                const unsigned vis = ((1u << width) - 1u) << lo_c;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = tb + 32 * k + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    s[r] = (key >= blo_v && key <= bhi_v) ? s[r] : kSent;
+                    const int c = 8 * (r >> 2) + (r & 3);
+                    // bit c sign-extended to all ones or zero; an opaque value, so the
+                    // select stays one bitfield insert instead of a compare and a select
+                    unsigned keep;
+                    asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(vis), "n"(c));
+                    s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (__float_as_uint(kSent) & ~keep));
                 }
             }
             float mt = kSent;
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
                                                                  false, false);
                 mt = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), kSent);
             }
-            const bool move = seen ? mt > kLazy : mt > kSent;
+            const bool move = mt > thr;
             if (__builtin_amdgcn_ballot_w64(move) != 0) {   // a query's first keys, or a jump of 2^kLazy
                 float delta = 0.f, alpha = 1.f;
                 if (move) {
@@ -335,14 +349,14 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
                     const float mhi = __uint_as_float(hi << 16);
                     const uint32_t lo = to_bf16(mnew - mhi);
                     const float mt_ref = mhi + __uint_as_float(lo << 16);
-                    alpha = seen ? fast_exp2(mref - mt_ref) : 0.f;
+                    alpha = thr > kSent ? fast_exp2(mref - mt_ref) : 0.f;
 #pragma unroll
                     for (int d = 0; d < 2; ++d)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
                     delta = mt_ref - mref;
                     mref = mt_ref;
-                    seen = true;
+                    thr = kLazy;
                     const uint32_t neg = (hi ^ 0x8000u) | ((lo ^ 0x8000u) << 16);
                     qext = __builtin_bit_cast(bf16x8_t, make_uint4(hf == 0 ? neg : 0u, 0u, 0u, 0u));
                 }
