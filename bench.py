@@ -242,16 +242,19 @@ def ring_words(desc) -> str:
     return f"{desc.ring_slots}-slot modulo ring (slot = position % {desc.ring_slots}, no compaction)"
 
 
-DEVICE_WARMUP_S = 0.3
+DEVICE_WARMUP_S = 0.5
 
 
 def device_warmup(seconds: float = None):
-    """Keep the GPU streaming HBM for `seconds` of wall time (the library's
-    read probe over a 1 GiB buffer, untimed) before the warmup steps: on a
-    freshly leased MI355X the first few hundred attention launches run about
-    6 % slower than the steady state (measured: 185 us with 5 warmup steps
-    against 173 us after 200), so a run with few warmup steps would time the
-    clock ramp instead of the kernel.  No state of the workload is touched."""
+    """Bring the GPU to its sustained clocks before the warmup steps: for
+    `seconds` of wall time, untimed, alternate the library's read probe over a
+    1 GiB buffer with bf16 8192 x 8192 products (torch.matmul).  On a freshly
+    leased MI355X the first attention launches run slower than the steady
+    state; on one box, 20 serving steps after 5 warmup steps took 175.9 and
+    178.3 us per launch (median) after a read-only warm-up, 171.3 and 171.9 us
+    after this mixed one, 171.9 us after 200 warmup steps instead, and 173.6 us
+    over 1000 steps.  A streaming read alone leaves the core clock low.  No
+    state of the workload is touched, and nothing of it is timed."""
     import torch
     import sliding_window_cached_amd as vrt
     seconds = DEVICE_WARMUP_S if seconds is None else seconds
@@ -259,13 +262,19 @@ def device_warmup(seconds: float = None):
         return
     buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(0)
+    a = torch.randn(8192, 8192, generator=gen, device="cuda:0").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, generator=gen, device="cuda:0").to(torch.bfloat16)
     stream = torch.cuda.current_stream().cuda_stream
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(16):
             vrt.read_probe(buf, buf.numel(), sink, stream)
+        for _ in range(8):
+            torch.matmul(a, b)
         torch.cuda.synchronize()
-    del buf, sink
+    del buf, sink, a, b
 
 
 class TimingEvent:
@@ -357,24 +366,26 @@ def bench_c2(args):
     Q, K, V = (_randn(gen, (total, S, 1, n, H, D), 0.5, dev) for _ in range(3))
     out = torch.empty((S, 1, n, H, D), dtype=torch.bfloat16, device=dev)
 
-    device_warmup()
-    for i in range(args.warmup):
-        vrt.enc_attn_feed(states, 0, 1, Q[i], K[i], V[i], n, out, stream)
-    torch.cuda.synchronize()
-
     # which timed steps compact (all rings share one schedule here) and the
-    # ring occupancy each step's attention sees
+    # ring occupancy each step's attention sees, from the ring model; and the
+    # timing events.  Worked out before the warmup steps, so that nothing
+    # leaves the GPU idle between them and the timed steps.
     _, nkv = states[0].query(0)
+    for i in range(args.warmup):
+        _, nkv, _ = vrt.ring_advance(desc, 0, nkv, n)
     compacting, nkv_seen = [], []
     for i in range(args.steps):
         _, nkv_after, nc = vrt.ring_advance(desc, 0, nkv, n)
         compacting.append(nc > 0)
         nkv_seen.append(nkv_after - n)
         nkv = nkv_after
-
     every = max(1, args.timing_every or (1 if args.steps < 100 else 10))
     timed = list(range(0, args.steps, every))
     ev = dict(zip(timed, _timing_events(len(timed))))
+
+    device_warmup()
+    for i in range(args.warmup):
+        vrt.enc_attn_feed(states, 0, 1, Q[i], K[i], V[i], n, out, stream)
     log(f"c2: timing {args.steps} steps (attention events on every {every})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -1335,8 +1346,8 @@ def main():
                     choices=["c1", "c2", "c2b", "c3", "c4", "cs", "cm", "copy", "read"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--device-warmup", type=float, default=DEVICE_WARMUP_S,
-                    help="seconds of untimed HBM streaming before the warmup steps (0: none; "
-                         "profiler runs use 0 to keep the trace small)")
+                    help="seconds of untimed HBM streaming and bf16 products before the warmup steps "
+                         "(0: none; profiler runs use 0 to keep the trace small)")
     ap.add_argument("--per-layer-steps", type=int, default=50,
                     help="c1: also time this many steps as 32 per-layer calls (0: skip; "
                          "profiler runs skip them)")
