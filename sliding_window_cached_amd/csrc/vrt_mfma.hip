@@ -342,6 +342,11 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
             }
             const bool move = mt > thr;
             if (__builtin_amdgcn_ballot_w64(move) != 0) {   // a query's first keys, or a jump of 2^kLazy
+                // a lane that had seen keys before rescales its sums; before
+                // its first visible key a lane's sums are exactly zero (every
+                // weight it added was 0), so a wave whose moving lanes all see
+                // their first keys skips the rescale
+                const bool jump = move && thr > kSent;
                 float delta = 0.f, alpha = 1.f;
                 if (move) {
                     const float mnew = mref + mt;
@@ -349,23 +354,25 @@ __global__ __launch_bounds__(256, 4) void k_attn_mfma(AttnArgs a, StateTable t) 
                     const float mhi = __uint_as_float(hi << 16);
                     const uint32_t lo = to_bf16(mnew - mhi);
                     const float mt_ref = mhi + __uint_as_float(lo << 16);
-                    alpha = thr > kSent ? fast_exp2(mref - mt_ref) : 0.f;
-#pragma unroll
-                    for (int d = 0; d < 2; ++d)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+                    if (jump) alpha = fast_exp2(mref - mt_ref);
                     delta = mt_ref - mref;
                     mref = mt_ref;
                     thr = kLazy;
                     const uint32_t neg = (hi ^ 0x8000u) | ((lo ^ 0x8000u) << 16);
                     qext = __builtin_bit_cast(bf16x8_t, make_uint4(hf == 0 ? neg : 0u, 0u, 0u, 0u));
                 }
-                // the denominators of queries jq and jq + 16 live in lane jq % 16
-                // (registers 0 and 1): rescaled with those queries' alpha,
-                // exchanged outside the divergent branch
-                const float a_lo = __shfl(alpha, lane & 15), a_hi = __shfl(alpha, (lane & 15) + 16);
-                den[0] *= a_lo;
-                den[1] *= a_hi;
+                if (__builtin_amdgcn_ballot_w64(jump) != 0) {
+#pragma unroll
+                    for (int d = 0; d < 2; ++d)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+                    // the denominators of queries jq and jq + 16 live in lane
+                    // jq % 16 (registers 0 and 1): rescaled with those queries'
+                    // alpha, exchanged outside the divergent branch
+                    const float a_lo = __shfl(alpha, lane & 15), a_hi = __shfl(alpha, (lane & 15) + 16);
+                    den[0] *= a_lo;
+                    den[1] *= a_hi;
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[r] -= delta;
             }
