@@ -50,7 +50,7 @@ def test_lookahead_chunkings_offline_and_oracle(dtype, left, right, d):
     desc = vrt.lookahead_desc(left, right, dtype=dtype, n_layers=L, heads=H, head_dim=d)
     q, k, v = seqs(90 + right, S, L, T, H, d, 1.0, dtype)
     qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
-    starts = [3, 123_456]
+    starts = [3, 2 ** 31 - T]   # the second stream ends at the largest position accepted
     runs = {}
     for sizes in ([4], [1], [7], [64], [512]):
         pool = Pool(desc, S, starts)
