@@ -1190,25 +1190,28 @@ def bench_c3(args):
             "parallelism": "none (1 GPU)", "device_warmup_s": DEVICE_WARMUP_S,
         },
         "roofline": {
-            "bound": "mfma",
+            "bound": "hbm",
             "kernel": "k_attn_mfma (matrix path: S^T = K Q^T and O^T += V^T P^T on "
                       "v_mfma_f32_32x32x16_bf16)",
-            "achieved": tflops,
-            "peak": MFMA_BF16_PEAK_TFS,
-            "unit": "TFLOP/s",
-            "frac": tflops / MFMA_BF16_PEAK_TFS,
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
             "traffic": (measured_traffic("k_attn_mfma", workload_key(args, "c3")) or {}).get("bytes"),
+            "bytes_model": "fused minimum per unit-batch (n q rows + 2 (old + n) K/V rows + n out rows) "
+                           "* H * d * 2 B, old = min(n_kv, 749)",
             "alg_flops_per_launch_full_window": full[0][1] if full else None,
             "launch_us_mean": t_attn / len(attn_ms) * 1e6,
             "launch_us_mean_full_window": (sum(a for a, _ in full) / len(full) * 1e3) if full else None,
             "launches_timed": len(attn_ms),
-            "hbm_achieved_gbs": gbs,
-            "hbm_frac": gbs / HBM_PEAK_GBS,
+            "mfma_achieved_tflops": tflops,
+            "mfma_frac": tflops / MFMA_BF16_PEAK_TFS,
             "mfma_busy_counter": measured_mfma_busy("k_attn_mfma", workload_key(args, "c3")),
             "band_efficiency": sum(v for v, _ in band) / sum(c for _, c in band),
-            "note": "algorithmic flops = 4*d*H per (query, visible key); the kernel is "
-                    "HBM-bound at the roofline (about 216 flop/B < the 312 flop/B ridge); "
-                    "mfma_busy_counter = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 "
+            "note": "the binding roof is HBM: the fused minimum bytes take longer at 8 TB/s than the "
+                    "algorithmic flops (4*d*H per (query, visible key)) at 2.5 PFLOP/s, about 216 flop/B "
+                    "against the 312 flop/B bf16 ridge; mfma_frac is the flop rate against the bf16 peak "
+                    "and mfma_busy_counter = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 "
                     "SIMDs) from the rocprofv3 counter run of the same workload; band_efficiency = "
                     "visible (query, key) pairs / pairs in the 32 x 32 score blocks the kernel computes",
         },
