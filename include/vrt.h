@@ -26,11 +26,13 @@
  * Conventions for every entry point
  * ---------------------------------
  * - All device pointers are caller-owned; the library never allocates or
- *   frees device memory and holds no state between calls apart from the
+ *   frees device memory (the one exception is the static 128 MiB partials
+ *   array of vrt_dec_attn_step_static, part of the loaded library on each
+ *   device it runs on) and holds no state between calls apart from the
  *   optional per-thread timing events of vrt_set_attn_events, the testing
- *   hook of vrt_test_launch_hook, and each device's compute-unit count and
- *   LDS size, read once.  All device work is enqueued on the caller's
- *   `stream` and is asynchronous.
+ *   hook of vrt_test_launch_hook, each device's compute-unit count and LDS
+ *   size, read once, and that array's address per device.  All device work
+ *   is enqueued on the caller's `stream` and is asynchronous.
  * - Arguments are checked before anything is enqueued.  On any error nothing
  *   is enqueued and no state changes (streaming-plan page, "Per-hook
  *   behavior": validate is pure).
