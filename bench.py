@@ -24,6 +24,8 @@ cs            the causal conv stem: 256 streams x 8 mel frames per step.
 cm            six (left, right)-window layers without RoPE (the moonshine pattern).
 copy          calibration copy of 1 GiB for the HBM byte counters.
 read          calibration: a plain streaming read of 4 GiB (the practical ceiling).
+gemm          calibration: the block's two projections at the serving shape, the library's
+              GEMM against the vendor BLAS (torch.matmul), each replayed from a HIP graph.
 
 --ring mod runs c1, c2 or c3 with the encoder cache kept as a modulo ring
 (1280 slots, slot = position % slots, no compaction; outputs bit-identical
@@ -951,6 +953,66 @@ def bench_read(args):
             "steps": args.steps, "kernel": "k_read_probe (vrt_read_probe)"}
 
 
+def bench_gemm(args):
+    """Calibration: the block's two projections at the serving shape (1024
+    rows = 256 streams x 4 frames, dim 1280, bf16, no bias or residual) on
+    the library's GEMM (vrt_linear, the kernel vrt_enc_block_feed runs) and
+    on the vendor BLAS (torch.matmul, hipBLASLt).  Each side's `steps`
+    launches are captured in one HIP graph and replayed, so the events time
+    the kernels back to back, not the Python launch path."""
+    import statistics
+    import torch
+    import sliding_window_cached_amd as vrt
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    M, K = 1024, 1280
+    device_warmup()
+    rows = []
+    for name, N in (("q/k/v", 3 * K), ("output", K)):
+        A = _randn(gen, (M, K), 1.0, dev)
+        Wm = _randn(gen, (N, K), 0.03, dev)
+        outs = {t: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for t in ("library", "vendor")}
+
+        def library():
+            vrt.linear(A, M, K, Wm, N, None, None, outs["library"], torch.cuda.current_stream().cuda_stream)
+
+        def vendor():
+            torch.matmul(A, Wm.t(), out=outs["vendor"])
+
+        us = {}
+        for tag, fn in (("library", library), ("vendor", vendor)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(args.steps):
+                    fn()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = []
+            for _ in range(5):
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                reps.append(e0.elapsed_time(e1) * 1e3 / args.steps)
+            us[tag] = statistics.median(reps)
+        diff = (outs["library"].float() - outs["vendor"].float()).abs().max().item()
+        flops = 2.0 * M * N * K
+        rows.append({"product": name, "M": M, "N": N, "K": K,
+                     "library_us": us["library"], "vendor_us": us["vendor"],
+                     "library_tflops": flops / us["library"] / 1e6, "vendor_tflops": flops / us["vendor"] / 1e6,
+                     "max_abs_diff_vs_vendor": diff})
+    return {"metric": "projection GEMM time, library vs vendor BLAS (calibration)",
+            "value": sum(r["library_us"] for r in rows), "unit": "us (q/k/v + output)",
+            "higher_is_better": False, "vendor_us": sum(r["vendor_us"] for r in rows),
+            "steps": args.steps, "warmup": args.warmup, "products": rows,
+            "kernels": "k_gemm (vrt_linear) and the hipBLASLt kernels torch.matmul picks"}
+
+
 def bench_c1(args):
     """64 streams x 32 independent layer caches, bf16 N(0,1)*0.5.  Stream i
     first ingests o_i ~ U{0..749} frames (one untimed catch-up feed) so ring
@@ -1346,7 +1408,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
     ap.add_argument("--config", default="c2",
-                    choices=["c1", "c2", "c2b", "c3", "c4", "cs", "cm", "copy", "read"])
+                    choices=["c1", "c2", "c2b", "c3", "c4", "cs", "cm", "copy", "read", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--device-warmup", type=float, default=DEVICE_WARMUP_S,
                     help="seconds of untimed HBM streaming and bf16 products before the warmup steps "
@@ -1377,6 +1439,11 @@ def main():
         args.steps = 20 if args.steps is None else args.steps
         args.warmup = 2 if args.warmup is None else args.warmup
         print(json.dumps(bench_read(args)), flush=True)
+        return
+    if args.config == "gemm":
+        args.steps = 50 if args.steps is None else args.steps
+        args.warmup = 5 if args.warmup is None else args.warmup
+        print(json.dumps(bench_gemm(args)), flush=True)
         return
     if args.config == "c2":
         args.steps = 1000 if args.steps is None else args.steps
