@@ -252,7 +252,7 @@ def device_warmup(seconds: float = None):
     `seconds` of wall time, untimed, alternate the library's read probe over a
     1 GiB buffer with bf16 8192 x 8192 products (torch.matmul).  On a freshly
     leased MI355X the first attention launches run slower than the steady
-    state; on one box, 20 serving steps after 5 warmup steps took 175.9 and
+    state; on one machine, 20 serving steps after 5 warmup steps took 175.9 and
     178.3 us per launch (median) after a read-only warm-up, 171.3 and 171.9 us
     after this mixed one, 171.9 us after 200 warmup steps instead, and 173.6 us
     over 1000 steps.  A streaming read alone leaves the core clock low.  No
