@@ -24,6 +24,7 @@ cs            the causal conv stem: 256 streams x 8 mel frames per step.
 cm            six (left, right)-window layers without RoPE (the moonshine pattern).
 copy          calibration copy of 1 GiB for the HBM byte counters.
 read          calibration: a plain streaming read of 4 GiB (the practical ceiling).
+stream        calibration: the serving step's tile stream with no arithmetic, and its L2 rate per CU.
 gemm          calibration: the block's two projections at the serving shape, the library's
               GEMM against the vendor BLAS (torch.matmul), each replayed from a HIP graph.
 
@@ -953,6 +954,57 @@ def bench_read(args):
             "steps": args.steps, "kernel": "k_read_probe (vrt_read_probe)"}
 
 
+def bench_stream(args):
+    """Calibration: the vector attention kernel's tile stream with none of
+    its arithmetic (vrt_tile_stream_probe).  (1) The serving step's shape:
+    1024 workgroups, five heads each, 12 tiles of 8 KB K + 8 KB V per head,
+    regions laid out like the rings (K and V 196608 bytes apart, heads
+    393216 apart), read once per launch from HBM with that kernel's
+    non-temporal loads.  (2) The same loop over 16 regions of 64 KB that stay
+    in L2, 200 passes, plain loads (as the GEMMs'), at 1, 2 and 4 workgroups
+    per CU: the L2 -> LDS rate per CU."""
+    import torch
+    import sliding_window_cached_amd as vrt
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    device_warmup()
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    n_wg, heads, tiles, stride, kv_off = 1024, 5, 12, 393216, 196608
+    nbytes = n_wg * heads * stride
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    t = timed(lambda: vrt.tile_stream_probe(buf, nbytes, n_wg, heads, tiles, n_wg * heads, stride, kv_off, 1,
+                                            sink, stream), args.steps)
+    moved = n_wg * heads * tiles * 16384
+    del buf
+    small = torch.ones(16 * 65536, dtype=torch.uint8, device=dev)
+    per_cu = {}
+    for wpc in (1, 2, 4):
+        passes = 200
+        ts = timed(lambda: vrt.tile_stream_probe(small, small.numel(), 256 * wpc, 1, 4, 16, 65536, 32768, passes,
+                                                 sink, stream, nontemporal=False), max(2, args.steps // 5))
+        per_cu[str(wpc)] = 256 * wpc * 4 * 16384 * passes / ts / 256 / 1e9
+    return {"metric": "attention tile-stream rate without arithmetic (calibration)", "value": moved / t / 1e9,
+            "unit": "GB/s", "frac_of_nominal": moved / t / 1e9 / HBM_PEAK_GBS, "us_per_launch": t * 1e6,
+            "bytes_per_launch": moved, "steps": args.steps,
+            "serving_shape": {"workgroups": n_wg, "heads_per_workgroup": heads, "tiles_per_head": tiles,
+                              "tile_bytes": 16384, "lds_stages": 2},
+            "l2_resident_gbs_per_cu_by_workgroups_per_cu": per_cu,
+            "kernel": "k_tile_probe (vrt_tile_stream_probe)"}
+
+
 def bench_gemm(args):
     """Calibration: the block's two projections at the serving shape (1024
     rows = 256 streams x 4 frames, dim 1280, bf16, no bias or residual) on
@@ -1408,7 +1460,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="default: c2 1000, c3 300")
     ap.add_argument("--warmup", type=int, default=None, help="default: c2 20, c3 30")
     ap.add_argument("--config", default="c2",
-                    choices=["c1", "c2", "c2b", "c3", "c4", "cs", "cm", "copy", "read", "gemm"])
+                    choices=["c1", "c2", "c2b", "c3", "c4", "cs", "cm", "copy", "read", "gemm", "stream"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--device-warmup", type=float, default=DEVICE_WARMUP_S,
                     help="seconds of untimed HBM streaming and bf16 products before the warmup steps "
@@ -1439,6 +1491,11 @@ def main():
         args.steps = 20 if args.steps is None else args.steps
         args.warmup = 2 if args.warmup is None else args.warmup
         print(json.dumps(bench_read(args)), flush=True)
+        return
+    if args.config == "stream":
+        args.steps = 20 if args.steps is None else args.steps
+        args.warmup = 2 if args.warmup is None else args.warmup
+        print(json.dumps(bench_stream(args)), flush=True)
         return
     if args.config == "gemm":
         args.steps = 50 if args.steps is None else args.steps

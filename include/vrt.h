@@ -422,6 +422,24 @@ vrt_status vrt_conv_stem_feed(vrt_conv_stem* const* stems, int n_stems, const vo
  * survey's advice: confirm the constants with measured kernels). */
 vrt_status vrt_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 
+/* Measurement only: the vector attention kernel's tile stream with none of
+ * its arithmetic, to set its HBM rate beside vrt_read_probe's ceiling
+ * (flags 1: the non-temporal loads that kernel uses; flags 0: plain loads,
+ * as the GEMMs use, e.g. for a stream kept in L2).  Other flag bits are
+ * invalid.
+ * n_wg workgroups; workgroup w reads regions (w * heads + h) mod n_regions,
+ * h < heads, region r starting at buf + r * region_stride: from each,
+ * `tiles` consecutive 8 KB K tiles and the 8 KB tiles kv_off bytes further
+ * on (its V rows), a 16 KB tile at a time through two LDS stages with one
+ * workgroup barrier per tile, `passes` times over.  Writes nothing but,
+ * never in practice, one word to sink (4-byte aligned).  buf 16-byte
+ * aligned, region_stride and kv_off multiples of 16, every byte read below
+ * buf + bytes, all counts >= 1; else VRT_ERR_INVALID.  A small n_regions
+ * keeps the stream in L2. */
+vrt_status vrt_tile_stream_probe(const void* buf, size_t bytes, int n_wg, int heads, int tiles, int n_regions,
+                                 size_t region_stride, size_t kv_off, int passes, int flags, void* sink,
+                                 hipStream_t stream);
+
 /* Per-component timing (the pages time each stage of a streamed feed on its
  * own: family doc, Capability Validation table, Streaming row, items 7 and
  * 8).  While both events are non-null, every later call on this thread

@@ -33,7 +33,7 @@ EXPORTS = (
     "vrt_rmsnorm", "vrt_linear", "vrt_block_workspace_bytes", "vrt_enc_block_feed",
     "vrt_conv_stem_device_bytes", "vrt_conv_stem_create", "vrt_conv_stem_reset",
     "vrt_conv_stem_destroy", "vrt_conv_stem_query", "vrt_conv_out_frames",
-    "vrt_conv_workspace_bytes", "vrt_conv_stem_feed", "vrt_read_probe", "vrt_attn_plan",
+    "vrt_conv_workspace_bytes", "vrt_conv_stem_feed", "vrt_read_probe", "vrt_tile_stream_probe", "vrt_attn_plan",
     "vrt_test_launch_hook", "vrt_test_launch_count", "vrt_dec_attn_step_static",
 )
 
@@ -168,6 +168,8 @@ def _load():
         "vrt_conv_out_frames": (c_int, [P, c_int]),
         "vrt_conv_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
         "vrt_read_probe": (c_int, [P, c_size_t, P, P]),
+        "vrt_tile_stream_probe": (c_int, [P, c_size_t, c_int, c_int, c_int, c_int, c_size_t, c_size_t, c_int, c_int,
+                                          P, P]),
         "vrt_attn_plan": (c_int, [POINTER(CacheDesc), c_int64, c_int, POINTER(c_int32),
                                   POINTER(c_int32), POINTER(c_int32)]),
         "vrt_test_launch_hook": (None, [c_int32, c_int32]),
@@ -441,6 +443,12 @@ def conv_stem_feed(stems, mel, n_frames, weights: ConvWeights, out, workspace, w
 
 def read_probe(buf, nbytes, sink, stream=0):
     _check(lib.vrt_read_probe(_ptr(buf), nbytes, _ptr(sink), stream), "read_probe")
+
+
+def tile_stream_probe(buf, nbytes, n_wg, heads, tiles, n_regions, region_stride, kv_off, passes, sink, stream=0,
+                      nontemporal=True):
+    _check(lib.vrt_tile_stream_probe(_ptr(buf), nbytes, n_wg, heads, tiles, n_regions, region_stride, kv_off,
+                                     passes, 1 if nontemporal else 0, _ptr(sink), stream), "tile_stream_probe")
 
 
 def set_attn_events(start=None, stop=None):

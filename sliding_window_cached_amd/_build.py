@@ -53,7 +53,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(out_dir, exist_ok=True)
     objs = []
     for src, is_hip in (("vrt_host.cpp", False), ("vrt_kernels.hip", True), ("vrt_mfma.hip", True),
-                        ("vrt_block.hip", True)):
+                        ("vrt_block.hip", True), ("vrt_probe.hip", True)):
         obj = os.path.join(out_dir, src + ".o")
         cmd = [hipcc, "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
         cmd += (["-x", "hip"] + DEVICE) if is_hip else ["-D__HIP_PLATFORM_AMD__"]

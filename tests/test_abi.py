@@ -327,6 +327,24 @@ def test_read_probe_argument_checks():
     assert vrt.lib.vrt_read_probe(P, 1 << 20, None, None) == vrt.ERR_INVALID
 
 
+def test_tile_stream_probe_argument_checks():
+    P = FAKE
+    f = vrt.lib.vrt_tile_stream_probe
+    big = 1 << 40
+    # buf, bytes, n_wg, heads, tiles, n_regions, region_stride, kv_off, passes, flags, sink, stream
+    assert f(None, big, 1, 1, 1, 1, 0, 8192, 1, 1, P, None) == vrt.ERR_INVALID
+    assert f(P + 8, big, 1, 1, 1, 1, 0, 8192, 1, 1, P, None) == vrt.ERR_INVALID
+    assert f(P, big, 1, 1, 1, 1, 0, 8192, 1, 1, None, None) == vrt.ERR_INVALID
+    for n_wg, heads, tiles, n_regions, passes in ((0, 1, 1, 1, 1), (1, 0, 1, 1, 1), (1, 1, 0, 1, 1),
+                                                  (1, 1, 1, 0, 1), (1, 1, 1, 1, 0)):
+        assert f(P, big, n_wg, heads, tiles, n_regions, 0, 8192, passes, 1, P, None) == vrt.ERR_INVALID
+    assert f(P, big, 1, 1, 1, 1, 8, 8192, 1, 1, P, None) == vrt.ERR_INVALID       # stride not 16-aligned
+    assert f(P, big, 1, 1, 1, 1, 0, 8200, 1, 1, P, None) == vrt.ERR_INVALID       # kv_off not 16-aligned
+    assert f(P, big, 1, 1, 1, 1, 0, 8192, 1, 2, P, None) == vrt.ERR_INVALID       # unknown flag
+    # the last byte read is region 3's V half, end of tile 2: 3 * 65536 + 32768 + 3 * 8192 = 253952
+    assert f(P, 253951, 1, 1, 3, 4, 65536, 32768, 1, 0, P, None) == vrt.ERR_INVALID
+
+
 def test_lookahead_host_rules():
     """ENC_LOOKAHEAD descs: no rotation (rope_theta 0), the ring must hold
     window + F + max_batch - 1 rows (F = lookahead - 1 future frames), a
