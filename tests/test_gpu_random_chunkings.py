@@ -11,7 +11,9 @@ vector path, 4-frame feeds.  Sizes cross the 512-frame split, and the
 sequences cross compactions of the 1536-slot ring at unaligned start
 positions; the modulo ring must give the same bits as the compacting ring
 (streaming plan, "Unbounded length" and SHIPPED, Verification: incremental
-equals offline)."""
+equals offline).  The lookahead windows and the conv stem get the same
+treatment (moonshine map, "Per-layer sliding-window mask"; streaming plan,
+"Chunk alignment")."""
 import numpy as np
 import pytest
 import torch
@@ -128,3 +130,84 @@ def test_bf16_matrix_path_random_chunkings_equal_offline(seed):
                     assert np.array_equal(out[s, l], refs[s][l]), (name, seed, trial, s, l, sizes)
     for pool in pools.values():
         pool.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_lookahead_random_chunkings_equal_offline(seed):
+    """(left, right) windows without rotation always take the vector kernel,
+    so any schedule of feed sizes answers each query with the offline pass's
+    bits (the moonshine streaming head: 8 x 40, windows (16, 4))."""
+    S, L, T, H, d, right = 2, 2, 700, 8, 40, 4
+    rng = np.random.default_rng([seed, 14])
+    starts = [int(x) for x in rng.integers(0, 1_000_000, S)]
+    desc = vrt.lookahead_desc(16, right, dtype=vrt.BF16, n_layers=L, heads=H, head_dim=d)
+    q, k, v = seqs(70 + seed, S, L, T, H, d, 1.0, vrt.BF16)
+    qd, kd, vd = (to_dev(x, vrt.BF16) for x in (q, k, v))
+    f = right - 1
+    refs = [[offline(desc, qd[s, l], kd[s, l], vd[s, l], T, starts[s])[:T - f] for l in range(L)]
+            for s in range(S)]
+    for trial in range(3):
+        sizes = random_sizes(rng, 1, 300, T)
+        say(f"lookahead seed {seed} trial {trial}: {len(sizes)} feeds")
+        pool = Pool(desc, S, starts)
+        states = [pool.states[i] for i in range(S)]
+        outs, t = [], 0
+        for m in sizes:
+            m = min(m, T - t)
+            _, nkv = states[0].query(0)
+            n_out = vrt.attn_out_frames(desc, nkv, m)
+            qc, kc, vc = (x[:, :, t:t + m].contiguous() for x in (qd, kd, vd))
+            oc = torch.empty_like(qc)
+            vrt.enc_attn_feed(states, 0, L, qc, kc, vc, m, oc, stream())
+            if n_out:
+                outs.append(oc[:, :, :n_out].clone())
+            t += m
+        torch.cuda.synchronize()
+        got = host(torch.cat(outs, dim=2))
+        pool.close()
+        for s in range(S):
+            for l in range(L):
+                assert np.array_equal(got[s, l], refs[s][l]), (seed, trial, s, l, sizes)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_conv_stem_random_chunkings_equal_one_feed(seed):
+    """The causal conv stem: every output row's k order is fixed, so any
+    schedule of mel chunk sizes (odd ones change how many conv0 frames are
+    carried between feeds) gives the one-feed bits."""
+    import synth
+    n_mel, dm, S, T = 128, 1280, 2, 90
+    rng = np.random.default_rng([seed, 15])
+    w = synth.conv_weights(72 + seed, n_mel, dm)
+    bfd = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+    tap_major = lambda W_: np.ascontiguousarray(np.transpose(W_, (0, 2, 1)).reshape(W_.shape[0], -1))
+    tens = {"w0": bfd(tap_major(w["w0"])), "b0": bfd(w["b0"]), "w1": bfd(tap_major(w["w1"])), "b1": bfd(w["b1"])}
+    cw = vrt.conv_weights(tens["w0"], tens["b0"], tens["w1"], tens["b1"])
+    mel = bfd(np.stack([synth.mel_frames(73 + seed, s, T, n_mel) for s in range(S)]))
+    nb = vrt.conv_stem_device_bytes(n_mel, dm)
+
+    def run(sizes):
+        mem = torch.empty(S * nb, dtype=torch.uint8, device=DEV)
+        stems = [vrt.ConvStem(n_mel, dm, mem[i * nb:(i + 1) * nb], nb) for i in range(S)]
+        outs, t = [], 0
+        for m in sizes:
+            m = min(m, T - t)
+            n_out = stems[0].out_frames(m)
+            wsb = vrt.conv_workspace_bytes(n_mel, dm, S, m)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+            o = torch.empty((S, max(n_out, 1), dm), dtype=torch.bfloat16, device=DEV)
+            assert vrt.conv_stem_feed(stems, mel[:, t:t + m].contiguous(), m, cw, o, ws, wsb, stream()) == n_out
+            if n_out:
+                outs.append(o[:, :n_out].clone())
+            t += m
+        torch.cuda.synchronize()
+        res = host(torch.cat(outs, dim=1))
+        for st in stems:
+            st.close()
+        return res
+
+    ref = run([T])
+    for trial in range(3):
+        sizes = random_sizes(rng, 1, 25, T)
+        say(f"conv stem seed {seed} trial {trial}: sizes {sizes}")
+        assert np.array_equal(run(sizes), ref), (seed, trial, sizes)
