@@ -211,3 +211,55 @@ def test_conv_stem_random_chunkings_equal_one_feed(seed):
         sizes = random_sizes(rng, 1, 25, T)
         say(f"conv stem seed {seed} trial {trial}: sizes {sizes}")
         assert np.array_equal(run(sizes), ref), (seed, trial, sizes)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_block_random_chunkings(seed):
+    """The attention half of an encoder block (RMSNorm, q/k/v, the path,
+    output projection and residual): the norm and projections are row-local
+    and the projections' k order is fixed, so after the same 750-frame
+    pre-fill any schedule of feeds under 32 frames reproduces 4-frame feeds,
+    and any schedule that keeps every sub-batch on the matrix path
+    reproduces 512-frame feeds, bit for bit, across compactions."""
+    import synth
+    from oracle import block
+    S, T, dim = 2, 1700, 1280
+    rng = np.random.default_rng([seed, 16])
+    starts = [int(x) for x in rng.integers(0, 1_000_000, S)]
+    wts = synth.block_weights(80 + seed, 0, dim)
+    bfd = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+    wd = {k: bfd(v) for k, v in wts.items()}
+    w_qkv = torch.cat([wd["wq"], wd["wk"], wd["wv"]], 0).contiguous()
+    bw = vrt.block_weights(wd["norm_w"], w_qkv, wd["bq"], wd["bv"], wd["wo"], wd["bo"], block.EPS)
+    xd = bfd(np.stack([synth.block_input(81 + seed, s, 0, T, dim) for s in range(S)]))
+    desc = vrt.enc_desc(dtype=vrt.BF16, n_layers=1)
+
+    def run(sizes):
+        pool = Pool(desc, S, starts)
+        out = torch.empty_like(xd)
+        t = 0
+        for m in sizes:
+            m = min(m, T - t)
+            if m <= 0:
+                break
+            wsb = vrt.block_workspace_bytes(desc, S * m)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+            xc = xd[:, t:t + m].contiguous()
+            oc = torch.empty_like(xc)
+            vrt.enc_block_feed(pool.states, 0, xc, m, bw, oc, ws, wsb, stream())
+            out[:, t:t + m] = oc
+            t += m
+        assert t == T
+        torch.cuda.synchronize()
+        pool.close()
+        return host(out)
+
+    vec_ref = run([750] + [4] * 238)
+    mat_ref = run([512] * 4)
+    for trial in range(2):
+        vs = [750] + random_sizes(rng, 1, 31, T - 750)
+        say(f"block seed {seed} trial {trial}: vector-path feeds after the pre-fill ({len(vs) - 1})")
+        assert np.array_equal(run(vs), vec_ref), (seed, trial, vs)
+        ms = matrix_sizes(rng, T)
+        say(f"block seed {seed} trial {trial}: matrix-path feeds {ms}")
+        assert np.array_equal(run(ms), mat_ref), (seed, trial, ms)
