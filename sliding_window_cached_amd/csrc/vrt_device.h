@@ -39,6 +39,18 @@ __device__ __forceinline__ void gst(void* p, T v) {
     typedef typename Raw<sizeof(T)>::T R;
     *(VRT_GLOBAL R*)(__UINTPTR_TYPE__)p = __builtin_bit_cast(R, v);
 }
+// A store with the non-temporal hint.  The vector attention kernel writes the
+// rows it appends this way: it reads them back through its own tile stream,
+// and on the 256-stream serving step ordinary stores of those 5 MB of rows
+// made the launch 6 % slower.  The separate append kernel and the compaction
+// copy keep ordinary stores: the attention launch right after them reads
+// their rows, and the hint made that catch-up step 2-3 % slower.  Ordering and
+// visibility are those of any other store.
+template <class T>
+__device__ __forceinline__ void gst_nt(void* p, T v) {
+    typedef typename Raw<sizeof(T)>::T R;
+    __builtin_nontemporal_store(__builtin_bit_cast(R, v), (VRT_GLOBAL R*)(__UINTPTR_TYPE__)p);
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -167,6 +179,14 @@ template <> __device__ __forceinline__ void st4<BF16T, true>(char* p, const floa
 }
 template <> __device__ __forceinline__ void st4<BF16T, false>(char* p, const float (&x)[4]) {
     *(uint2*)p = pack_bf16x4(x);
+}
+// Four consecutive elements in the storage type, stored with gst_nt.
+template <class E> __device__ __forceinline__ void st4_ring(char* p, const float (&x)[4]);
+template <> __device__ __forceinline__ void st4_ring<F32T>(char* p, const float (&x)[4]) {
+    gst_nt<float4>(p, make_float4(x[0], x[1], x[2], x[3]));
+}
+template <> __device__ __forceinline__ void st4_ring<BF16T>(char* p, const float (&x)[4]) {
+    gst_nt<uint2>(p, pack_bf16x4(x));
 }
 
 template <int CPR>

@@ -370,17 +370,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         st4<E, false>(dst + 4 * c * E::E, y0);
         st4<E, false>(dst + (H2 + 4 * c) * E::E, y1);
         if (APPEND && !LOOK && appender && gh == 0) {
+            // the new rows go out with the non-temporal hint (st4_ring, gst_nt)
             char* Kg = layer + (long long)g * a.g.slice_bytes;
             char* Vg = Kg + a.g.v_off;
             const long long slot = MOD ? (pos % a.g.slots) : (long long)(nkv + j);
 #pragma unroll
             for (int q = 0; q < 4; ++q) rope_pair(it.k0[q], it.k1[q], an[q], &y0[q], &y1[q]);
             char* kd = Kg + slot * L::RB;
-            st4<E, true>(kd + 4 * c * E::E, y0);
-            st4<E, true>(kd + (H2 + 4 * c) * E::E, y1);
+            st4_ring<E>(kd + 4 * c * E::E, y0);
+            st4_ring<E>(kd + (H2 + 4 * c) * E::E, y1);
 #pragma unroll
             for (int u = 0; u < L::CPR / CG; ++u)
-                gst<uint4>(Vg + slot * L::RB + 16 * (c + u * CG), it.vch[u]);
+                gst_nt<uint4>(Vg + slot * L::RB + 16 * (c + u * CG), it.vch[u]);
         }
     };
     Item first;
