@@ -234,14 +234,15 @@ int pick_hg(const Geom& g, long long units, int rows_per_head, long long qchunks
     int cus, lds;
     device_props(&cus, &lds);
     const int elem = g.dtype == 1 ? 2 : 4;
-    const long long wg_lds = (long long)attn_stages(g.dtype, g.D, splits > 1) * 2 * kTile * g.D * elem +
-                             kQsBytes + 4 * kTile * elem;
+    const int qs = attn_qs_bytes(g.D * elem);
+    const long long wg_lds = (long long)attn_stages(g.dtype, g.D, splits > 1) * 2 * kTile * g.D * elem + qs +
+                             4 * kTile * elem;
     const long long per_cu = std::max(1LL, std::min(4LL, lds / wg_lds));
     const long long target = per_cu * cus;
     int best = 1;
     for (int h = 2; h <= g.hkv; ++h) {
         if (g.hkv % h) continue;
-        if ((long long)h * rows_per_head * g.D * elem > kQsBytes) break;
+        if ((long long)h * rows_per_head * g.D * elem > qs) break;
         if (units * (g.hkv / h) * qchunks * splits < target) break;
         best = h;
     }

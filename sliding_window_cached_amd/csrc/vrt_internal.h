@@ -38,8 +38,12 @@ constexpr int kMaxCompact = 256;
 constexpr int kTile = 64;
 // Query rows (q head x position) of one kv head in one attention workgroup.
 constexpr int kRows = 16;
-// LDS bytes for the rotated query rows of a workgroup's kv-head group.
+// LDS bytes for the rotated query rows of a workgroup's kv-head group: 6 KB,
+// or more when kRows rows of one head are wider than that (fp32 rows of
+// head_dim 128, 16 x 512 bytes).  The attention kernel also stages its output
+// rows there.
 constexpr int kQsBytes = 6144;
+constexpr int attn_qs_bytes(int row_bytes) { return kRows * row_bytes > kQsBytes ? kRows * row_bytes : kQsBytes; }
 // Sub-batches of at least this many frames take the matrix-core path (bf16,
 // head_dim 64, one query head per kv head); smaller ones the VALU path.
 constexpr int kMfmaMinFrames = 32;

@@ -201,7 +201,7 @@ struct Tl {
     static constexpr int IPW = CPR / 4;          // DMA instructions per wave per K (or V) tile
     static constexpr int LPW = 2 * IPW;          // DMA instructions per wave per tile
     static constexpr int PRB = kTile * E::E;     // bytes of one P row
-    static constexpr int QCAP = kQsBytes;        // rotated query rows of the head group
+    static constexpr int QCAP = attn_qs_bytes(RB);   // rotated query rows of the head group
     static constexpr int BYTES = NST * 2 * TILE + QCAP + 4 * PRB;
 };
 // RPW: rows per wave (1 when a head has at most 4 rows; then the wave's query
@@ -609,9 +609,23 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
                     }
 #pragma unroll
                     for (int k = 0; k < DPL; ++k) gst<float>(pr + 2 + lane + 64 * k, acc[i][k]);
+                } else if constexpr (!LOOK) {
+                    // the output row goes to this wave's own query row of the
+                    // head, which nothing reads any more; the workgroup writes
+                    // all of them after the last head
+                    char* srow = Qs + (hh * R + r) * L::RB;
+#pragma unroll
+                    for (int k = 0; k < DPL; ++k) {
+                        const float o = acc[i][k] / lrow;
+                        const int d = lane + 64 * k;
+                        if constexpr (E::E == 2)
+                            *(uint16_t*)(srow + 2 * d) = (uint16_t)to_bf16(o);
+                        else
+                            *(float*)(srow + 4 * d) = o;
+                    }
                 } else {
                     const int hq = g * group + gh;
-                    const long long orow = (LOOK ? (long long)a.look_o0 : (long long)m.t0) + (long long)qc * a.qchunk + j;
+                    const long long orow = (long long)a.look_o0 + (long long)qc * a.qchunk + j;
                     char* dst = (char*)a.out + ((cu * m.n_total + orow) * a.g.hq + hq) * (long long)Dio * E::E;
 #pragma unroll
                     for (int k = 0; k < DPL; ++k) {
@@ -625,6 +639,24 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
                     }
                 }
             }
+        }
+    }
+
+    // ---- outputs: 16-byte stores of the staged rows.  The rows of query j
+    // for the group's heads are adjacent in `out` (q heads g0 * group onwards),
+    // so consecutive threads write consecutive bytes.  Written once at the end
+    // instead of one 2- or 4-byte element per lane at each head's end: on the
+    // 256-stream serving step that made the launch 2 % faster.
+    if constexpr (!SPLIT && !LOOK) {
+        __syncthreads();   // every wave's output rows are in Qs
+        const long long orow0 = (long long)m.t0 + (long long)qc * a.qchunk;
+        for (int x = threadIdx.x; x < hg * R * L::CPR; x += blockDim.x) {
+            const int c = x % L::CPR, rest = x / L::CPR;
+            const int gh = rest % group, hh = (rest / group) % hg, j = rest / (group * hg);
+            const uint4 v = *(const uint4*)(Qs + (hh * R + j * group + gh) * L::RB + 16 * c);
+            char* dst = (char*)a.out +
+                        ((cu * m.n_total + orow0 + j) * a.g.hq + (long long)(g0 + hh) * group + gh) * (long long)L::RB;
+            gst<uint4>(dst + 16 * c, v);
         }
     }
 }
