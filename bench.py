@@ -1441,7 +1441,7 @@ def bench_c4(args):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_attn split-K (kv heads x 1024-key splits) + k_dec_combine",
+            "kernel": "k_attn split-K (kv heads x 2048-key splits) + k_dec_combine",
             "achieved": gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -291,7 +291,7 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* states, int n_states, int 
  * up).  The same kernels and arithmetic as vrt_dec_attn_step, so the outputs
  * are bit-identical.  n_tok = 1 needs vrt_dec_workspace_bytes(desc,
  * n_states, n_layers, 1) <= 128 MiB (VRT_ERR_CAPACITY otherwise; the
- * 32-stream x 26-layer step at window 8192 needs 118.8 MiB); n_tok > 1 (a
+ * 32-stream x 26-layer step at window 8192 needs 69.1 MiB); n_tok > 1 (a
  * prefill) uses no partials.  Nothing in the array has to start at zero:
  * the merge reads only the splits the same call wrote.  Every call on one
  * device shares that device's array and it keeps the last call's contents,

@@ -751,8 +751,8 @@ size_t vrt_dec_workspace_bytes(const vrt_cache_desc* desc, int n_states, int n_l
     if (n_tok > 1) return 0;  // prefill needs no workspace
     const size_t n_splits = (size_t)(desc->window + kSplitLen - 2) / kSplitLen + 1;
     const size_t group = desc->n_heads_q / desc->n_heads_kv;
-    return (size_t)n_states * n_layers * desc->n_heads_kv * n_splits * group *
-           (2 + desc->head_dim) * sizeof(float);
+    return (size_t)n_states * n_layers * desc->n_heads_kv * n_splits *
+           (size_t)dec_record_floats((int)group, desc->head_dim) * sizeof(float);
 }
 
 vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int layer0,

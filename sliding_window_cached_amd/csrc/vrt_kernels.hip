@@ -215,6 +215,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     using L = Tl<E, D, attn_stages(E::E == 2 ? 1 : 0, D, SPLIT)>;
     constexpr int H2 = D / 2, CG = H2 / 4, DPL = D / 64;
     __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+    // split mode: (m, l) of every row of the group's heads, written out as one
+    // 128-byte line per head after the last head
+    __shared__ float mls[SPLIT ? 2 * (L::QCAP / L::RB) : 1];
     char* Qs = lds + L::NST * 2 * L::TILE;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -601,14 +604,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
                 const float lrow = wave_sum(lpart[i]);
                 const int j = r / group, gh = r - j * group;
                 if (SPLIT) {
-                    float* pr = a.partials +
-                                (((cu * a.g.hkv + g) * a.n_splits + split) * group + r) * (long long)(2 + D);
+                    float* rec = a.partials + ((cu * a.g.hkv + g) * a.n_splits + split) * dec_record_floats(group, D);
                     if (lane == 0) {
-                        gst<float>(pr, mrow[i]);
-                        gst<float>(pr + 1, lrow);
+                        mls[(hh * R + r) * 2] = mrow[i];
+                        mls[(hh * R + r) * 2 + 1] = lrow;
                     }
 #pragma unroll
-                    for (int k = 0; k < DPL; ++k) gst<float>(pr + 2 + lane + 64 * k, acc[i][k]);
+                    for (int k = 0; k < DPL; ++k) gst_nt<float>(rec + kMlFloats + r * D + lane + 64 * k, acc[i][k]);
                 } else if constexpr (!LOOK) {
                     // the output row goes to this wave's own query row of the
                     // head, which nothing reads any more; the workgroup writes
@@ -647,6 +649,15 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
     // so consecutive threads write consecutive bytes.  Written once at the end
     // instead of one 2- or 4-byte element per lane at each head's end: on the
     // 256-stream serving step that made the launch 2 % faster.
+    if constexpr (SPLIT) {
+        // the (m, l) line of each head's record: 2 R values, then zeros
+        __syncthreads();   // every wave's (m, l) are in mls
+        for (int x = threadIdx.x; x < hg * kMlFloats; x += blockDim.x) {
+            const int hh = x / kMlFloats, f = x - hh * kMlFloats;
+            float* rec = a.partials + ((cu * a.g.hkv + g0 + hh) * a.n_splits + split) * dec_record_floats(group, D);
+            gst_nt<float>(rec + f, f < 2 * R ? mls[hh * 2 * R + f] : 0.f);
+        }
+    }
     if constexpr (!SPLIT && !LOOK) {
         __syncthreads();   // every wave's output rows are in Qs
         const long long orow0 = (long long)m.t0 + (long long)qc * a.qchunk;
@@ -706,18 +717,19 @@ __global__ __launch_bounds__(64) void k_dec_combine(AttnArgs a, StateTable t) {
     const long long wlo = max(avail, pq - a.g.window + 1);
     const int ns = (int)(floor_div(pq, a.split_len) - floor_div(wlo, a.split_len) + 1);
     const int group = a.g.group;
-    const float* base = a.partials + ((cu * a.g.hkv + g) * a.n_splits) * group * (long long)(2 + D);
+    const long long rec = dec_record_floats(group, D);
+    const float* base = a.partials + ((cu * a.g.hkv + g) * a.n_splits) * rec;
     float M = kSent;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, gld<float>(base + ((long long)s * group + r) * (2 + D)));
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, gld<float>(base + s * rec + 2 * r));
     float Lsum = 0.f, o[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) o[k] = 0.f;
     for (int s = 0; s < ns; ++s) {
-        const float* pr = base + ((long long)s * group + r) * (2 + D);
-        const float w = fast_exp2(gld<float>(pr) - M);
-        Lsum = __fmaf_rn(gld<float>(pr + 1), w, Lsum);
+        const float* pr = base + s * rec;
+        const float w = fast_exp2(gld<float>(pr + 2 * r) - M);
+        Lsum = __fmaf_rn(gld<float>(pr + 2 * r + 1), w, Lsum);
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) o[k] = __fmaf_rn(gld<float>(pr + 2 + lane + 64 * k), w, o[k]);
+        for (int k = 0; k < DPL; ++k) o[k] = __fmaf_rn(gld<float>(pr + kMlFloats + r * D + lane + 64 * k), w, o[k]);
     }
     char* dst = (char*)a.out + ((cu * m.n_total + m.t0) * a.g.hq + hq) * (long long)D * E::E;
 #pragma unroll

@@ -17,9 +17,9 @@ def test_decoder_single_token_splits_the_window():
     desc = vrt.dec_desc()
     for u in UNITS:
         hg, splits, qc = vrt.attn_plan(desc, u, 1)
-        # window 8192 in absolute-aligned spans of 1024 keys: 8 full spans
+        # window 8192 in absolute-aligned spans of 2048 keys: 4 full spans
         # plus the one the window's ragged start falls in
-        assert splits == 9 and qc == 1
+        assert splits == 5 and qc == 1
         assert hg >= 1 and 8 % hg == 0
 
 
