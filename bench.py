@@ -960,9 +960,12 @@ def bench_stream(args):
     1024 workgroups, five heads each, 12 tiles of 8 KB K + 8 KB V per head,
     regions laid out like the rings (K and V 196608 bytes apart, heads
     393216 apart), read once per launch from HBM with that kernel's
-    non-temporal loads.  (2) The same loop over 16 regions of 64 KB that stay
-    in L2, 200 passes, plain loads (as the GEMMs'), at 1, 2 and 4 workgroups
-    per CU: the L2 -> LDS rate per CU."""
+    non-temporal loads.  (2) The same workgroups over a 753-key window as the
+    kernel reads it: 13 tiles per head, the first read from row 32 and the
+    last up to row 16, the other rows of those two tiles fetching the nearest
+    row read (753 rows of K and V per head).  (3) The loop of (1) over 16
+    regions of 64 KB that stay in L2, 200 passes, plain loads (as the GEMMs'),
+    at 1, 2 and 4 workgroups per CU: the L2 -> LDS rate per CU."""
     import torch
     import sliding_window_cached_amd as vrt
     dev = torch.device("cuda:0")
@@ -988,6 +991,10 @@ def bench_stream(args):
     t = timed(lambda: vrt.tile_stream_probe(buf, nbytes, n_wg, heads, tiles, n_wg * heads, stride, kv_off, 1,
                                             sink, stream), args.steps)
     moved = n_wg * heads * tiles * 16384
+    tw = timed(lambda: vrt.tile_stream_probe(buf, nbytes, n_wg, heads, 13, n_wg * heads, stride, kv_off, 1, sink,
+                                             stream, first_row=32, last_row=16), args.steps)
+    rows = 32 + 11 * 64 + 17
+    moved_w = n_wg * heads * rows * 256
     del buf
     small = torch.ones(16 * 65536, dtype=torch.uint8, device=dev)
     per_cu = {}
@@ -1001,6 +1008,11 @@ def bench_stream(args):
             "bytes_per_launch": moved, "steps": args.steps,
             "serving_shape": {"workgroups": n_wg, "heads_per_workgroup": heads, "tiles_per_head": tiles,
                               "tile_bytes": 16384, "lds_stages": 2},
+            "window_753_rows": {"tiles_per_head": 13, "first_row": 32, "last_row": 16, "rows_per_head": rows,
+                                "us_per_launch": tw * 1e6, "bytes_of_rows_read": moved_w,
+                                "gbs_of_rows_read": moved_w / tw / 1e9,
+                                "note": "13 steps per head like the serving kernel's unaligned window; if the time "
+                                        "follows the rows read and not the steps, this matches the 12-tile rate"},
             "l2_resident_gbs_per_cu_by_workgroups_per_cu": per_cu,
             "kernel": "k_tile_probe (vrt_tile_stream_probe)"}
 

@@ -431,14 +431,18 @@ vrt_status vrt_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t
  * h < heads, region r starting at buf + r * region_stride: from each,
  * `tiles` consecutive 8 KB K tiles and the 8 KB tiles kv_off bytes further
  * on (its V rows), a 16 KB tile at a time through two LDS stages with one
- * workgroup barrier per tile, `passes` times over.  Writes nothing but,
- * never in practice, one word to sink (4-byte aligned).  buf 16-byte
- * aligned, region_stride and kv_off multiples of 16, every byte read below
- * buf + bytes, all counts >= 1; else VRT_ERR_INVALID.  A small n_regions
- * keeps the stream in L2. */
+ * workgroup barrier per tile, `passes` times over.  The first tile of each
+ * region is read from its row first_row on, the last up to its row last_row
+ * (rows are 128 bytes, 64 to a tile); rows outside fetch the nearest row read,
+ * as the attention kernel's tiles at a window's edges do (0 and 63: whole
+ * tiles).  Writes nothing but, never in practice, one word to sink (4-byte
+ * aligned).  buf 16-byte aligned, region_stride and kv_off multiples of 16,
+ * every byte read below buf + bytes, all counts >= 1, 0 <= first_row,
+ * last_row <= 63 and, for one tile, first_row <= last_row; else
+ * VRT_ERR_INVALID.  A small n_regions keeps the stream in L2. */
 vrt_status vrt_tile_stream_probe(const void* buf, size_t bytes, int n_wg, int heads, int tiles, int n_regions,
-                                 size_t region_stride, size_t kv_off, int passes, int flags, void* sink,
-                                 hipStream_t stream);
+                                 size_t region_stride, size_t kv_off, int passes, int first_row, int last_row,
+                                 int flags, void* sink, hipStream_t stream);
 
 /* Per-component timing (the pages time each stage of a streamed feed on its
  * own: family doc, Capability Validation table, Streaming row, items 7 and

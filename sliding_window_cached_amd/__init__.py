@@ -169,7 +169,7 @@ def _load():
         "vrt_conv_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
         "vrt_read_probe": (c_int, [P, c_size_t, P, P]),
         "vrt_tile_stream_probe": (c_int, [P, c_size_t, c_int, c_int, c_int, c_int, c_size_t, c_size_t, c_int, c_int,
-                                          P, P]),
+                                          c_int, c_int, P, P]),
         "vrt_attn_plan": (c_int, [POINTER(CacheDesc), c_int64, c_int, POINTER(c_int32),
                                   POINTER(c_int32), POINTER(c_int32)]),
         "vrt_test_launch_hook": (None, [c_int32, c_int32]),
@@ -446,9 +446,10 @@ def read_probe(buf, nbytes, sink, stream=0):
 
 
 def tile_stream_probe(buf, nbytes, n_wg, heads, tiles, n_regions, region_stride, kv_off, passes, sink, stream=0,
-                      nontemporal=True):
+                      nontemporal=True, first_row=0, last_row=63):
     _check(lib.vrt_tile_stream_probe(_ptr(buf), nbytes, n_wg, heads, tiles, n_regions, region_stride, kv_off,
-                                     passes, 1 if nontemporal else 0, _ptr(sink), stream), "tile_stream_probe")
+                                     passes, first_row, last_row, 1 if nontemporal else 0, _ptr(sink), stream),
+           "tile_stream_probe")
 
 
 def set_attn_events(start=None, stop=None):

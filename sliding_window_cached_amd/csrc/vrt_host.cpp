@@ -1190,10 +1190,13 @@ vrt_status vrt_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t
 }
 
 vrt_status vrt_tile_stream_probe(const void* buf, size_t bytes, int n_wg, int heads, int tiles, int n_regions,
-                                 size_t region_stride, size_t kv_off, int passes, int flags, void* sink,
-                                 hipStream_t stream) {
+                                 size_t region_stride, size_t kv_off, int passes, int first_row, int last_row,
+                                 int flags, void* sink, hipStream_t stream) {
     if (!buf || !sink || !aligned16(buf) || ((uintptr_t)sink & 3) || n_wg < 1 || heads < 1 || tiles < 1 ||
         n_regions < 1 || passes < 1 || region_stride % 16 || kv_off % 16 || (flags & ~1))
+        return VRT_ERR_INVALID;
+    if (first_row < 0 || first_row >= kTile || last_row < 0 || last_row >= kTile ||
+        (tiles == 1 && first_row > last_row))
         return VRT_ERR_INVALID;
     // the last byte read: region n_regions - 1, its V half, the end of tile `tiles` - 1
     const long double last = (long double)(n_regions - 1) * region_stride + kv_off + (long double)tiles * 8192;
@@ -1201,7 +1204,8 @@ vrt_status vrt_tile_stream_probe(const void* buf, size_t bytes, int n_wg, int he
         return VRT_ERR_INVALID;
     clear_sticky_error();
     return note(launch_tile_probe((const char*)buf, (long long)region_stride, (long long)kv_off, n_regions, n_wg,
-                                  heads, tiles, passes, (flags & 1) != 0, (unsigned*)sink, stream)) == hipSuccess
+                                  heads, tiles, passes, first_row, last_row, (flags & 1) != 0, (unsigned*)sink,
+                                  stream)) == hipSuccess
                ? VRT_OK
                : VRT_ERR_DEVICE;
 }

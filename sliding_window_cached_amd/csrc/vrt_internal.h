@@ -258,7 +258,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, const RowCopyArgs* tail
                        const RowCopyTable* tail_t = nullptr);
 hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 hipError_t launch_tile_probe(const char* buf, long long region_stride, long long kv_off, int n_regions, int n_wg,
-                             int heads, int tiles, int passes, bool nt, unsigned* sink, hipStream_t s);
+                             int heads, int tiles, int passes, int row_lo, int row_hi, bool nt, unsigned* sink,
+                             hipStream_t s);
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
 

@@ -56,11 +56,14 @@ __device__ __forceinline__ void wait_vm0() {
 // V tiles kv_off bytes further on, a 16 KB tile at a time, through two LDS
 // stages with one workgroup barrier per tile and the same DMA
 // (global_load_lds_dwordx4, with that kernel's non-temporal hint when NT),
-// `passes` times over.
+// `passes` times over.  The first tile of a region is read from row row_lo
+// and the last up to row row_hi; rows outside fetch the nearest row read, as
+// the attention kernel's edge tiles do (row_lo 0, row_hi 63: whole tiles).
 template <bool NT>
 __global__ __launch_bounds__(256) void k_tile_probe(const char* __restrict__ buf, long long region_stride,
                                                     long long kv_off, int n_regions, int heads, int tiles,
-                                                    int passes, unsigned magic, unsigned* sink) {
+                                                    int passes, int row_lo, int row_hi, unsigned magic,
+                                                    unsigned* sink) {
     __shared__ __attribute__((aligned(16))) char lds[2 * 16384];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -69,14 +72,19 @@ __global__ __launch_bounds__(256) void k_tile_probe(const char* __restrict__ buf
     // counters, so a tile's issue is a few scalar adds)
     const int r0 = (int)(((long long)blockIdx.x * heads) % n_regions);
     int reg = r0, it = 0;
-    const char* lane_k = buf + (wave * 2) * 1024 + lane * 16;
+    // the lane's 16-byte chunk: row wave * 16 + lane / 8 (+ 8 in the second
+    // instruction) of the 64-row tile, chunk lane % 8 of the 128-byte row
+    const int row0 = wave * 16 + (lane >> 3);
+    const char* lane_k = buf + (lane & 7) * 16;
     auto issue = [&](int st) {
         const char* k = lane_k + (long long)reg * region_stride + (long long)it * 8192;
         char* l = lds + st * 16384 + wave * 2 * 1024;
+        const int rlo = it == 0 ? row_lo : 0, rhi = it == tiles - 1 ? row_hi : 63;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {   // 8 instructions of 1 KB per half tile, 2 per wave
-            dma16_hint<NT>(k + i * 1024, l + i * 1024);
-            dma16_hint<NT>(k + kv_off + i * 1024, l + 8192 + i * 1024);
+            const int rr = min(max(row0 + 8 * i, rlo), rhi);   // 0 <= rr <= 63
+            dma16_hint<NT>(k + rr * 128, l + i * 1024);
+            dma16_hint<NT>(k + kv_off + rr * 128, l + 8192 + i * 1024);
         }
         if (++it == tiles) {
             it = 0;
@@ -99,13 +107,14 @@ __global__ __launch_bounds__(256) void k_tile_probe(const char* __restrict__ buf
 }  // namespace
 
 hipError_t launch_tile_probe(const char* buf, long long region_stride, long long kv_off, int n_regions, int n_wg,
-                             int heads, int tiles, int passes, bool nt, unsigned* sink, hipStream_t s) {
+                             int heads, int tiles, int passes, int row_lo, int row_hi, bool nt, unsigned* sink,
+                             hipStream_t s) {
     if (nt)
         VRT_LAUNCH(k_tile_probe<true>, dim3((unsigned)n_wg), dim3(256), 0, s, buf, region_stride, kv_off, n_regions,
-                   heads, tiles, passes, 0x9e3779b9u, sink);
+                   heads, tiles, passes, row_lo, row_hi, 0x9e3779b9u, sink);
     else
         VRT_LAUNCH(k_tile_probe<false>, dim3((unsigned)n_wg), dim3(256), 0, s, buf, region_stride, kv_off, n_regions,
-                   heads, tiles, passes, 0x9e3779b9u, sink);
+                   heads, tiles, passes, row_lo, row_hi, 0x9e3779b9u, sink);
     return hipSuccess;
 }
 

@@ -331,18 +331,22 @@ def test_tile_stream_probe_argument_checks():
     P = FAKE
     f = vrt.lib.vrt_tile_stream_probe
     big = 1 << 40
-    # buf, bytes, n_wg, heads, tiles, n_regions, region_stride, kv_off, passes, flags, sink, stream
-    assert f(None, big, 1, 1, 1, 1, 0, 8192, 1, 1, P, None) == vrt.ERR_INVALID
-    assert f(P + 8, big, 1, 1, 1, 1, 0, 8192, 1, 1, P, None) == vrt.ERR_INVALID
-    assert f(P, big, 1, 1, 1, 1, 0, 8192, 1, 1, None, None) == vrt.ERR_INVALID
+    # buf, bytes, n_wg, heads, tiles, n_regions, region_stride, kv_off, passes, first_row, last_row, flags, sink,
+    # stream
+    assert f(None, big, 1, 1, 1, 1, 0, 8192, 1, 0, 63, 1, P, None) == vrt.ERR_INVALID
+    assert f(P + 8, big, 1, 1, 1, 1, 0, 8192, 1, 0, 63, 1, P, None) == vrt.ERR_INVALID
+    assert f(P, big, 1, 1, 1, 1, 0, 8192, 1, 0, 63, 1, None, None) == vrt.ERR_INVALID
     for n_wg, heads, tiles, n_regions, passes in ((0, 1, 1, 1, 1), (1, 0, 1, 1, 1), (1, 1, 0, 1, 1),
                                                   (1, 1, 1, 0, 1), (1, 1, 1, 1, 0)):
-        assert f(P, big, n_wg, heads, tiles, n_regions, 0, 8192, passes, 1, P, None) == vrt.ERR_INVALID
-    assert f(P, big, 1, 1, 1, 1, 8, 8192, 1, 1, P, None) == vrt.ERR_INVALID       # stride not 16-aligned
-    assert f(P, big, 1, 1, 1, 1, 0, 8200, 1, 1, P, None) == vrt.ERR_INVALID       # kv_off not 16-aligned
-    assert f(P, big, 1, 1, 1, 1, 0, 8192, 1, 2, P, None) == vrt.ERR_INVALID       # unknown flag
+        assert f(P, big, n_wg, heads, tiles, n_regions, 0, 8192, passes, 0, 63, 1, P, None) == vrt.ERR_INVALID
+    assert f(P, big, 1, 1, 1, 1, 8, 8192, 1, 0, 63, 1, P, None) == vrt.ERR_INVALID       # stride not 16-aligned
+    assert f(P, big, 1, 1, 1, 1, 0, 8200, 1, 0, 63, 1, P, None) == vrt.ERR_INVALID       # kv_off not 16-aligned
+    assert f(P, big, 1, 1, 1, 1, 0, 8192, 1, 0, 63, 2, P, None) == vrt.ERR_INVALID       # unknown flag
+    for first, last in ((-1, 63), (64, 63), (0, -1), (0, 64)):                           # rows outside a tile
+        assert f(P, big, 1, 1, 2, 1, 0, 16384, 1, first, last, 1, P, None) == vrt.ERR_INVALID
+    assert f(P, big, 1, 1, 1, 1, 0, 8192, 1, 40, 39, 1, P, None) == vrt.ERR_INVALID      # one tile, empty rows
     # the last byte read is region 3's V half, end of tile 2: 3 * 65536 + 32768 + 3 * 8192 = 253952
-    assert f(P, 253951, 1, 1, 3, 4, 65536, 32768, 1, 0, P, None) == vrt.ERR_INVALID
+    assert f(P, 253951, 1, 1, 3, 4, 65536, 32768, 1, 0, 63, 0, P, None) == vrt.ERR_INVALID
 
 
 def test_lookahead_host_rules():

@@ -35,9 +35,13 @@ def test_tile_stream_probe_reads_inside_its_buffer(n_wg, heads, tiles, n_regions
     say(f"tile stream probe: {n_wg} workgroups x {heads} heads x {tiles} tiles over {n_regions} regions "
         f"({need} bytes), {passes} passes")
     assert vrt.lib.vrt_tile_stream_probe(vrt._ptr(buf), need - 1, n_wg, heads, tiles, n_regions, stride, kv_off,
-                                         passes, 1, vrt._ptr(sink), stream()) == vrt.ERR_INVALID
+                                         passes, 0, 63, 1, vrt._ptr(sink), stream()) == vrt.ERR_INVALID
     for nt in (True, False):
         vrt.tile_stream_probe(buf, need, n_wg, heads, tiles, n_regions, stride, kv_off, passes, sink, stream(),
                               nontemporal=nt)
+    # a window's edge tiles: the first read from row 32, the last up to row 16 (one tile: rows 16..32)
+    first, last = (32, 16) if tiles > 1 else (16, 32)
+    vrt.tile_stream_probe(buf, need, n_wg, heads, tiles, n_regions, stride, kv_off, passes, sink, stream(),
+                          first_row=first, last_row=last)
     torch.cuda.synchronize()
     assert sink.cpu().tolist() == [0, 0, 0, 0]
