@@ -73,16 +73,26 @@ def test_random_subsets_batched_equal_serial(dtype, kind, seed):
     B.close()
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_decoder_random_subsets_batched_equal_serial(seed):
-    """Decoder states (GQA 32/8 x 128, window and ring 8192) prefilled to
-    random contexts below the window, then single-token steps on random
-    subsets and layer ranges: the batched call (its split-K plan takes kv
-    heads per workgroup from the call's size) equals each state stepped
-    alone, bit for bit, outputs and metadata."""
-    S, L, HQ, HK, DD = 6, 3, 32, 8, 128
+DEC_SHAPES = {   # q heads, kv heads, head_dim, dtype, window = ring
+    "32/8x128 bf16 w8192": (32, 8, 128, vrt.BF16, 8192),
+    "32/8x64 bf16 w2048": (32, 8, 64, vrt.BF16, 2048),
+    "16/4x64 fp32 w2048": (16, 4, 64, vrt.F32, 2048),
+}
+
+
+@pytest.mark.parametrize("seed, shape", [(0, "32/8x128 bf16 w8192"), (1, "32/8x128 bf16 w8192"),
+                                         (2, "32/8x64 bf16 w2048"), (3, "16/4x64 fp32 w2048")])
+def test_decoder_random_subsets_batched_equal_serial(seed, shape):
+    """Decoder states prefilled to random contexts below the window, then
+    single-token steps on random subsets and layer ranges: the batched call
+    (its split-K plan takes kv heads per workgroup from the call's size)
+    equals each state stepped alone, bit for bit, outputs and metadata."""
+    HQ, HK, DD, dtype, win = DEC_SHAPES[shape]
+    S, L = 6, 3
+    tdt = torch.bfloat16 if dtype == vrt.BF16 else torch.float32
     rng = np.random.default_rng([seed, 22])
-    desc = vrt.dec_desc(n_layers=L)
+    desc = vrt.dec_desc(dtype=dtype, n_layers=L, heads_q=HQ, heads_kv=HK, head_dim=DD, window=win,
+                        ring_slots=win)
     A, B = Pool(desc, S, [0] * S), Pool(desc, S, [0] * S)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(200 + seed)
@@ -96,10 +106,10 @@ def test_decoder_random_subsets_batched_equal_serial(seed):
         return out
 
     for i in range(S):
-        ctx = int(rng.integers(1, 8100))
-        say(f"state {i}: prefill {ctx} tokens")
-        q = draw(gen, (1, L, ctx, HQ, DD), torch.bfloat16)
-        k, v = (draw(gen, (1, L, ctx, HK, DD), torch.bfloat16) for _ in range(2))
+        ctx = int(rng.integers(1, win - 92))   # 8100 at window 8192, as before
+        say(f"{shape}: state {i}: prefill {ctx} tokens")
+        q = draw(gen, (1, L, ctx, HQ, DD), tdt)
+        k, v = (draw(gen, (1, L, ctx, HK, DD), tdt) for _ in range(2))
         step(A, [i], 0, L, q, k, v, ctx)
         step(B, [i], 0, L, q, k, v, ctx)
     for rnd in range(12):
@@ -107,8 +117,8 @@ def test_decoder_random_subsets_batched_equal_serial(seed):
         subset = sorted(int(x) for x in rng.choice(S, m, replace=False))
         l0 = int(rng.integers(0, L))
         nl = int(rng.integers(1, L - l0 + 1))
-        q = draw(gen, (m, nl, 1, HQ, DD), torch.bfloat16)
-        k, v = (draw(gen, (m, nl, 1, HK, DD), torch.bfloat16) for _ in range(2))
+        q = draw(gen, (m, nl, 1, HQ, DD), tdt)
+        k, v = (draw(gen, (m, nl, 1, HK, DD), tdt) for _ in range(2))
         out = step(A, subset, l0, nl, q, k, v, 1)
         for j, i in enumerate(subset):
             ref = step(B, [i], l0, nl, q[j:j + 1].contiguous(), k[j:j + 1].contiguous(),
