@@ -644,13 +644,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
         }
     }
 
-    // ---- outputs: 16-byte stores of the staged rows.  The rows of query j
-    // for the group's heads are adjacent in `out` (q heads g0 * group onwards),
-    // so consecutive threads write consecutive bytes.  Written once at the end
-    // instead of one 2- or 4-byte element per lane at each head's end: on the
-    // 256-stream serving step that made the launch 2 % faster.
+    // ---- split mode: the (m, l) line of each head's partial record, 2 R
+    // values then zeros, written whole
     if constexpr (SPLIT) {
-        // the (m, l) line of each head's record: 2 R values, then zeros
         __syncthreads();   // every wave's (m, l) are in mls
         for (int x = threadIdx.x; x < hg * kMlFloats; x += blockDim.x) {
             const int hh = x / kMlFloats, f = x - hh * kMlFloats;
@@ -658,6 +654,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, StateTable t) {
             gst_nt<float>(rec + f, f < 2 * R ? mls[hh * 2 * R + f] : 0.f);
         }
     }
+    // ---- outputs: 16-byte stores of the staged rows.  The rows of query j
+    // for the group's heads are adjacent in `out` (q heads g0 * group onwards),
+    // so consecutive threads write consecutive bytes.  Written once at the end
+    // instead of one 2- or 4-byte element per lane at each head's end: on the
+    // 256-stream serving step that made the launch 2 % faster.
     if constexpr (!SPLIT && !LOOK) {
         __syncthreads();   // every wave's output rows are in Qs
         const long long orow0 = (long long)m.t0 + (long long)qc * a.qchunk;
