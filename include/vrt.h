@@ -274,7 +274,9 @@ vrt_status vrt_ring_compact(vrt_stream_state* const* states, int n_states, int l
  * may not overwrite a slot that one of its own queries still needs
  * (VRT_ERR_INVALID).
  * q/out: [n_states][n_layers][n_tok][n_heads_q][head_dim]; k/v as for feed.
- * `workspace` (device, caller-owned) must hold vrt_dec_workspace_bytes. */
+ * `workspace` (device, caller-owned, 16-byte aligned; 128-byte alignment puts
+ * every split's partial record on whole cache lines) must hold
+ * vrt_dec_workspace_bytes; VRT_ERR_INVALID if it is null or misaligned. */
 size_t vrt_dec_workspace_bytes(const vrt_cache_desc* desc, int n_states, int n_layers,
                                int n_tok);
 vrt_status vrt_dec_attn_step(vrt_stream_state* const* states, int n_states, int layer0,

@@ -764,7 +764,7 @@ vrt_status vrt_dec_attn_step(vrt_stream_state* const* st, int n_states, int laye
     if (!q || !k || !v || !out || n_tok < 1) return VRT_ERR_INVALID;
     const vrt_cache_desc& d = st[0]->d;
     if (n_tok == 1) {
-        if (!workspace) return VRT_ERR_INVALID;
+        if (!workspace || ((uintptr_t)workspace & 15)) return VRT_ERR_INVALID;
         if (ws_bytes < vrt_dec_workspace_bytes(&d, n_states, n_layers, 1)) return VRT_ERR_CAPACITY;
     }
     // positions in range, and no sub-batch of a prefill overwrites a slot that

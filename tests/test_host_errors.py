@@ -217,3 +217,20 @@ def test_static_decode_step_host_logic():
     assert vrt.dec_attn_step_static(big, 0, 26, Q, K, V, 1, O, check=False) == vrt.ERR_CAPACITY
     assert vrt.test_launch_count() == 0 and big[0].query(0) == (0, 0)
     assert vrt.dec_attn_step_static(big[:32], 0, 26, Q, K, V, 1, O, check=False) == vrt.OK
+
+
+def test_decoder_workspace_must_be_16_byte_aligned():
+    """A decode step with a misaligned or missing workspace is refused before
+    anything is enqueued or any state moves; an aligned one goes through."""
+    d = vrt.dec_desc(n_layers=1)
+    sts = states_of(d, 2)
+    vrt.dec_attn_step(sts, 0, 1, Q, K, V, 39, O)
+    wsb = vrt.dec_workspace_bytes(d, 2, 1, 1)
+    for bad in (WS + 4, WS + 8, None):
+        vrt.test_launch_hook(0, dry_run=True)
+        assert vrt.dec_attn_step(sts, 0, 1, Q, K, V, 1, O, bad, wsb, check=False) == vrt.ERR_INVALID
+        assert vrt.test_launch_count() == 0
+        assert all(s.query(0) == (0, 39) for s in sts)
+    vrt.test_launch_hook(0, dry_run=True)
+    assert vrt.dec_attn_step(sts, 0, 1, Q, K, V, 1, O, WS + 16, wsb, check=False) == vrt.OK
+    assert vrt.test_launch_count() == 2 and all(s.query(0) == (0, 40) for s in sts)
