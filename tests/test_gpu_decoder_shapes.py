@@ -65,3 +65,48 @@ def test_decode_step_shapes(hq, hkv, d, dtype):
     assert np.array_equal(ring, lin), "ring and never-wrapping buffer differ"
     ref = attention.windowed(q, k, v, 0, W, THETA)
     check_close(ring, ref, dtype, what)
+
+
+def test_decode_step_group16_two_heads_per_workgroup():
+    """64 states x 8 layers of a 32/2 x 64 bf16 decoder (GQA group 16, 16
+    rows per kv head, four per wave): one batched decode step, which the
+    planner gives 2 kv heads per workgroup, equals the same step made state
+    by state (1 kv head per workgroup) bit for bit; sampled outputs match the
+    oracle."""
+    S, L, HQ, HK, DD, win = 64, 8, 32, 2, 64, 2048
+    desc = vrt.dec_desc(dtype=vrt.BF16, n_layers=L, heads_q=HQ, heads_kv=HK, head_dim=DD, window=win,
+                        ring_slots=win)
+    assert vrt.attn_plan(desc, S * L, 1)[0] == 2 and vrt.attn_plan(desc, L, 1)[0] == 1
+    rng = np.random.default_rng(44)
+    ctx = [int(c) for c in rng.integers(2, 300, S)]   # a prefill has 2 or more tokens
+    seqs = [qkv(500 + i, i, 0, (c + 1) * L, HQ, HK, DD, 1.0, "bf16") for i, c in enumerate(ctx)]
+    # per state: [L][c + 1][heads][d], token c is the decode step
+    seqs = [tuple(x.reshape(L, c + 1, x.shape[1], DD) for x in s) for s, c in zip(seqs, ctx)]
+    A, B = Pool(desc, S, [0] * S), Pool(desc, S, [0] * S)
+    ws_b = vrt.dec_workspace_bytes(desc, S, L, 1)
+    ws = torch.empty(ws_b // 4 + 1, dtype=torch.float32, device=DEV)
+    say(f"group 16: prefill {S} states x {L} layers to contexts {min(ctx)}..{max(ctx)}")
+    for i, c in enumerate(ctx):
+        q, k, v = (to_dev(x[:, :c][None], vrt.BF16) for x in seqs[i])
+        for pool in (A, B):
+            o = torch.empty_like(q)
+            vrt.dec_attn_step([pool.states[i]], 0, L, q, k, v, c, o, None, 0, stream())
+    qs, ks, vs = (torch.stack([to_dev(s[t][:, c:c + 1], vrt.BF16) for s, c in zip(seqs, ctx)])
+                  for t in range(3))
+    out = torch.empty_like(qs)
+    vrt.dec_attn_step(A.states, 0, L, qs, ks, vs, 1, out, ws, ws_b, stream())
+    torch.cuda.synchronize()
+    batched = host(out)
+    for i in range(S):
+        o = torch.empty_like(qs[i:i + 1])
+        vrt.dec_attn_step([B.states[i]], 0, L, qs[i:i + 1].contiguous(), ks[i:i + 1].contiguous(),
+                          vs[i:i + 1].contiguous(), 1, o, ws, ws_b, stream())
+        torch.cuda.synchronize()
+        assert np.array_equal(host(o)[0], batched[i]), ("state", i)
+    for i in range(0, S, 9):
+        for l in (0, L - 1):
+            q, k, v = (x[l] for x in seqs[i])
+            ref = attention.windowed_at(q, k, v, 0, win, THETA, [ctx[i]])
+            check_close(batched[i, l, 0][None], ref, vrt.BF16, f"group 16 state {i} layer {l}")
+    A.close()
+    B.close()
