@@ -221,3 +221,74 @@ def test_encoder_c1_shape_batched_equals_one_stream_at_a_time():
     for _, states in pools:
         for s in states:
             s.close()
+
+
+@pytest.mark.parametrize("dtype, n, S, hg_expect", [(vrt.F32, 8, 16, 2), (vrt.BF16, 16, 16, 2),
+                                                   (vrt.BF16, 8, 32, 5)])
+def test_encoder_multirow_feeds_batched_equals_one_stream_at_a_time(dtype, n, S, hg_expect):
+    """Vector-path feeds of 8 or 16 frames (8 or 16 query rows per head, four
+    per wave) across S streams x 8 layers, where the planner takes several kv
+    heads per workgroup: equal bit for bit to each stream fed alone (one head
+    per workgroup), across each stream's compaction; sampled rows against the
+    oracle."""
+    L, H, D, W, steps = 8, 20, 64, 750, 8
+    tdt = torch.bfloat16 if dtype == vrt.BF16 else torch.float32
+    desc = vrt.enc_desc(dtype=dtype, n_layers=L)
+    hg, _, _ = vrt.attn_plan(desc, S * L, n)
+    say(f"multi-row feeds: {n} frames, {S} streams x {L} layers, {hg} heads per workgroup")
+    assert hg == hg_expect and vrt.attn_plan(desc, L, n)[0] == 1
+    pre = [int(x) for x in offsets(61, S, 1536 - steps * n + 1, 1530)]   # each ring compacts inside the run
+    starts = [int(x) for x in offsets(62, S, 0, 10 ** 6)]
+    T = max(pre) + steps * n
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(61 + n + S)
+    q, k, v = ((torch.randn((S, L, T, H, D), generator=gen, device=DEV) * 0.5).to(tdt) for _ in range(3))
+    nb = vrt.state_device_bytes(desc)
+    pools = []
+    for _ in range(2):
+        mem = torch.empty(S * nb, dtype=torch.uint8, device=DEV)
+        pools.append((mem, [vrt.StreamState(desc, mem[j * nb:(j + 1) * nb], nb, starts[j]) for j in range(S)]))
+    st = stream()
+    for i in range(S):
+        qs, ks, vs = (x[i:i + 1, :, :pre[i]].contiguous() for x in (q, k, v))
+        o = torch.empty_like(qs)
+        for _, states in pools:
+            vrt.enc_attn_feed([states[i]], 0, L, qs, ks, vs, pre[i], o, st)
+    outs = [torch.empty((steps, S, L, n, H, D), dtype=tdt, device=DEV) for _ in range(2)]
+    for j in range(steps):
+        qs, ks, vs = (torch.stack([x[i, :, pre[i] + n * j:pre[i] + n * (j + 1)] for i in range(S)]).contiguous()
+                      for x in (q, k, v))
+        vrt.enc_attn_feed(pools[0][1], 0, L, qs, ks, vs, n, outs[0][j], st)
+        for i in range(S):
+            o = torch.empty_like(qs[i:i + 1])
+            vrt.enc_attn_feed([pools[1][1][i]], 0, L, qs[i:i + 1].contiguous(), ks[i:i + 1].contiguous(),
+                              vs[i:i + 1].contiguous(), n, o, st)
+            outs[1][j, i] = o[0]
+    torch.cuda.synchronize()
+    a, b = as_np(outs[0]), as_np(outs[1])
+    assert np.isfinite(a).all()
+    assert np.array_equal(a, b), "batched launch != one stream at a time"
+    for i in range(S):
+        r = EncRing()
+        r.reset(starts[i])
+        r.feed(pre[i])
+        for _ in range(steps):
+            r.feed(n)
+        assert r.events, ("no compaction", i)
+        for pool in pools:
+            assert pool[1][i].query(L - 1) == (r.abs_base, r.n_kv), i
+    jobs, where = [], []
+    for i in (0, S // 2, S - 1):
+        for l in (0, L - 1):
+            for j, f in ((0, 0), (steps - 1, n - 1)):
+                t = pre[i] + n * j + f
+                lo = max(0, t - W + 1)
+                jobs.append((as_np(q[i, l, lo:t + 1]), as_np(k[i, l, lo:t + 1]), as_np(v[i, l, lo:t + 1]),
+                             starts[i] + lo, W, t - lo))
+                where.append((i, l, j, f))
+    refs = oracle_rows(jobs)
+    got = np.stack([a[j, i, l, f] for i, l, j, f in where])
+    check_close(got, np.stack(refs), dtype, f"multi-row feeds {n} frames, sampled rows")
+    for _, states in pools:
+        for s in states:
+            s.close()
